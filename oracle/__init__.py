@@ -1,0 +1,39 @@
+"""CPU fp64 oracle for per-rank ring attention under the head-tail (zigzag) layout.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import, call or run
+anything in this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it. It shares no code with the HIP
+library (``context_ring_attention_zigzag_amd``) and imports nothing from it.
+
+Pages this oracle follows (cited by title and section):
+
+* "Context Parallelism" (Ultralytics glossary), sections "How context
+  parallelism works" and "Practical use and trade-offs".
+* "Context Parallelism v.s. Sequence Parallelism (Megatron-LM)"
+  (orangingq.tistory.com), sections "Context Parallelism (CP)" and
+  "Implementation quirk: symmetric chunk assignment".
+* "Sequence Parallelism and Ring Attention" (aiunderstanding.org), sections
+  "Deep dive", "Technical insight" and the FAQ.
+
+Every function here is pinned by ``tests/test_oracle.py`` to something other
+than itself (brute force, a library routine, closed forms, the pages' cp=4
+table). No function is "parity unpinned".
+"""
+
+from .ring_attention import (  # noqa: F401
+    CONTIGUOUS,
+    ZIGZAG,
+    allowed_mask,
+    causal_pairs_zigzag,
+    count_pairs,
+    finalize,
+    fold_block,
+    full_attention,
+    init_state,
+    layout,
+    merge,
+    padded_len,
+    rank_reference,
+    ring_emulation,
+    ring_source,
+)

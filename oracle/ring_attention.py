@@ -1,0 +1,303 @@
+"""Plain, slow, fp64 CPU definition of what one context-parallel rank computes.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never
+imports this module.
+
+Everything is numpy float64 with no blocking, fusion or reordering beyond what
+the pages state. Tensors are laid out [B, H, L, D] (sequence on dim 2, as in
+the SDPA call of "Context Parallelism", section "Practical use and
+trade-offs"). Positions are global token positions; -1 marks a pad token.
+
+Readings where the pages are silent (each also listed in the design notes):
+
+* softmax scale defaults to 1/sqrt(D) (the SDPA call on the glossary page
+  passes no scale, so the library default applies);
+* a key is allowed for a query iff both are real tokens and, when causal,
+  pos_k <= pos_q by *global* position (lower-triangular valid region,
+  "Implementation quirk: symmetric chunk assignment");
+* pad tokens go at the tail, carry position -1, are never attended, and a pad
+  query (or any query with no allowed key) yields O = 0 and LSE = -inf;
+* LSE is in natural-log units;
+* ring step t of rank r folds the block that started on rank (r - t) mod cp
+  (blocks move to the next device each hop).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+ZIGZAG = 0
+CONTIGUOUS = 1
+
+
+# ---------------------------------------------------------------------------
+# Layout: "Context Parallelism v.s. Sequence Parallelism (Megatron-LM)",
+# section "Implementation quirk: symmetric chunk assignment" (zigzag), and
+# "Sequence Parallelism and Ring Attention", section "Deep dive" (contiguous).
+# ---------------------------------------------------------------------------
+
+def padded_len(seq_len: int, cp: int, lay: int) -> int:
+    """Sequence length after padding.
+
+    Zigzag needs the sequence to split evenly into 2*cp chunks, so it pads up
+    to a multiple of 2*cp (Megatron page, symmetric chunk assignment). The
+    contiguous split only needs cp equal pieces.
+    """
+    if seq_len < 0 or cp < 1 or lay not in (ZIGZAG, CONTIGUOUS):
+        raise ValueError("bad layout arguments")
+    unit = 2 * cp if lay == ZIGZAG else cp
+    return ((seq_len + unit - 1) // unit) * unit
+
+
+def layout(seq_len: int, cp: int, lay: int):
+    """Rank-major token layout.
+
+    Returns ``(token_idx, pos_ids)``, both int64 of length S_pad. Entry
+    ``r*Lr + i`` (Lr = S_pad/cp) is the i-th local token of rank r.
+
+    Zigzag: the padded sequence is cut into 2*cp equal chunks of c tokens and
+    rank r holds chunk r followed by chunk 2*cp-1-r (the page's cp=4 table:
+    rank 0 has chunks 0 and 7, ..., rank 3 has chunks 3 and 4).
+    Contiguous: rank r holds tokens [r*Lr, (r+1)*Lr).
+    pos_ids is the global position of the token, or -1 for a pad token (the
+    page insists local positions are the global ones, never 0, 1, 2, ...).
+    """
+    s_pad = padded_len(seq_len, cp, lay)
+    lr = s_pad // cp
+    token_idx = np.empty(s_pad, dtype=np.int64)
+    if lay == ZIGZAG:
+        c = s_pad // (2 * cp)
+        for r in range(cp):
+            front, back = r, 2 * cp - 1 - r
+            token_idx[r * lr: r * lr + c] = np.arange(front * c, front * c + c)
+            token_idx[r * lr + c: (r + 1) * lr] = np.arange(back * c, back * c + c)
+    else:
+        token_idx[:] = np.arange(s_pad)
+    pos_ids = np.where(token_idx < seq_len, token_idx, -1)
+    return token_idx, pos_ids
+
+
+def ring_source(rank: int, t: int, cp: int) -> int:
+    """Rank whose KV block rank ``rank`` holds at ring step ``t``.
+
+    Each hop passes the block to the next device, so after t hops rank r holds
+    the block that started on rank r - t ("Context Parallelism", section "How
+    context parallelism works"; "Sequence Parallelism and Ring Attention",
+    "Deep dive").
+    """
+    return (rank - t) % cp
+
+
+# ---------------------------------------------------------------------------
+# Masking and plain attention.
+# ---------------------------------------------------------------------------
+
+def allowed_mask(q_pos, k_pos, causal: bool):
+    """[Nq, Nk] bool: may query i attend key j.
+
+    Causal attention keeps the lower-triangular region by global position,
+    diagonal included (Megatron page, symmetric chunk assignment; SDPA's
+    is_causal on the glossary page). Pad tokens (pos -1) take no part.
+    """
+    q_pos = np.asarray(q_pos)[:, None]
+    k_pos = np.asarray(k_pos)[None, :]
+    ok = (q_pos >= 0) & (k_pos >= 0)
+    if causal:
+        ok = ok & (k_pos <= q_pos)
+    return ok
+
+
+def _attend_rows(q, k, v, q_pos, k_pos, causal, scale):
+    """Softmax attention for a few query rows of one (b, h).
+
+    q [n, D], k/v [Nk, D], float64. Returns O [n, D], LSE [n]. This is the
+    textbook definition: s = scale * q k^T, masked softmax over keys, O = P v.
+    """
+    s = scale * (q @ k.T)
+    ok = allowed_mask(q_pos, k_pos, causal)
+    s = np.where(ok, s, -np.inf)
+    m = s.max(axis=1)
+    has = np.isfinite(m)
+    m_safe = np.where(has, m, 0.0)
+    p = np.where(ok, np.exp(s - m_safe[:, None]), 0.0)
+    l = p.sum(axis=1)
+    o = np.zeros((q.shape[0], v.shape[1]))
+    o[has] = (p[has] @ v) / l[has, None]
+    lse = np.full(q.shape[0], -np.inf)
+    lse[has] = m[has] + np.log(l[has])
+    return o, lse
+
+
+def full_attention(q, k, v, q_pos, k_pos, causal: bool, scale=None, row_chunk: int = 64):
+    """Unpartitioned softmax attention, fp64.
+
+    q [B, H, Nq, D], k/v [B, H, Nk, D]; q_pos [Nq], k_pos [Nk] global positions.
+    Returns O [B, H, Nq, D] float64 and LSE [B, H, Nq] float64.
+    This is the result ring attention must reproduce up to rounding
+    ("Context Parallelism", "How context parallelism works";
+    "Sequence Parallelism and Ring Attention", "Technical insight").
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    b_, h_, nq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    q_pos = np.asarray(q_pos)
+    k_pos = np.asarray(k_pos)
+    o = np.zeros((b_, h_, nq, v.shape[-1]))
+    lse = np.zeros((b_, h_, nq))
+    for b in range(b_):
+        for h in range(h_):
+            for r0 in range(0, nq, row_chunk):
+                r1 = min(nq, r0 + row_chunk)
+                o[b, h, r0:r1], lse[b, h, r0:r1] = _attend_rows(
+                    q[b, h, r0:r1], k[b, h], v[b, h], q_pos[r0:r1], k_pos, causal, scale)
+    return o, lse
+
+
+def rank_reference(q, k, v, seq_len: int, cp: int, lay: int, rank: int, causal: bool,
+                   scale=None, rows=None):
+    """What rank ``rank`` must output: rows of full attention over the whole sequence.
+
+    q, k, v are the unsharded [B, H, seq_len, D] tensors in natural token
+    order. The rank's local rows come from ``layout``; ``rows`` optionally
+    picks a subset of local row indices (for sampled checks at large sizes).
+    Returns O [B, H, n, D] and LSE [B, H, n] in local order.
+    """
+    token_idx, pos_ids = layout(seq_len, cp, lay)
+    lr = len(token_idx) // cp
+    local_tok = token_idx[rank * lr:(rank + 1) * lr]
+    local_pos = pos_ids[rank * lr:(rank + 1) * lr]
+    if rows is not None:
+        rows = np.asarray(rows)
+        local_tok = local_tok[rows]
+        local_pos = local_pos[rows]
+    q = np.asarray(q, dtype=np.float64)
+    d = q.shape[-1]
+    # A pad query reads a zero row; allowed_mask gives it no keys anyway.
+    qsel = np.zeros(q.shape[:2] + (len(local_tok), d))
+    real = local_tok < seq_len
+    qsel[:, :, real] = q[:, :, local_tok[real]]
+    k_pos = np.arange(seq_len)
+    return full_attention(qsel, k, v, local_pos, k_pos, causal, scale)
+
+
+# ---------------------------------------------------------------------------
+# Blockwise (ring) computation with online softmax:
+# "Sequence Parallelism and Ring Attention", "Deep dive" and "Technical
+# insight": keep a running max and a running normaliser, rescale the earlier
+# partial sums whenever a larger score shows up.
+# ---------------------------------------------------------------------------
+
+def init_state(b_: int, h_: int, lq: int, d: int):
+    """Running state before any block: O = 0 (unnormalised), m = -inf, l = 0."""
+    return (np.zeros((b_, h_, lq, d)), np.full((b_, h_, lq), -np.inf), np.zeros((b_, h_, lq)))
+
+
+def fold_block(state, q, k_blk, v_blk, q_pos, k_pos, causal: bool, scale=None):
+    """Fold one arriving KV block into the running (O, m, l).
+
+    m is the running max of the allowed scaled scores (natural-log units), l
+    the running sum of exp(score - m), O the running sum of exp(score - m) * v.
+    With m_new = max(m, block max), earlier sums are rescaled by exp(m - m_new).
+    A row with nothing allowed so far keeps m = -inf, l = 0, O = 0.
+    """
+    o, m, l = (np.array(x, dtype=np.float64) for x in state)
+    q = np.asarray(q, dtype=np.float64)
+    k_blk = np.asarray(k_blk, dtype=np.float64)
+    v_blk = np.asarray(v_blk, dtype=np.float64)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    ok = allowed_mask(q_pos, k_pos, causal)
+    b_, h_ = q.shape[:2]
+    for b in range(b_):
+        for h in range(h_):
+            s = np.where(ok, scale * (q[b, h] @ k_blk[b, h].T), -np.inf)
+            m_new = np.maximum(m[b, h], s.max(axis=1))
+            fin = np.isfinite(m_new)
+            m_use = np.where(fin, m_new, 0.0)
+            alpha = np.where(np.isfinite(m[b, h]), np.exp(m[b, h] - m_use), 0.0)
+            p = np.where(ok, np.exp(s - m_use[:, None]), 0.0)
+            l[b, h] = alpha * l[b, h] + p.sum(axis=1)
+            o[b, h] = alpha[:, None] * o[b, h] + p @ v_blk[b, h]
+            m[b, h] = m_new
+    return o, m, l
+
+
+def merge(state1, state2):
+    """Combine two partial states over disjoint key sets.
+
+    The same rescaling rule as ``fold_block``, applied to two already-reduced
+    partials: m = max(m1, m2), each side scaled by exp(m_i - m).
+    """
+    o1, m1, l1 = (np.asarray(x, dtype=np.float64) for x in state1)
+    o2, m2, l2 = (np.asarray(x, dtype=np.float64) for x in state2)
+    m = np.maximum(m1, m2)
+    m_use = np.where(np.isfinite(m), m, 0.0)
+    a1 = np.where(np.isfinite(m1), np.exp(m1 - m_use), 0.0)
+    a2 = np.where(np.isfinite(m2), np.exp(m2 - m_use), 0.0)
+    return a1[..., None] * o1 + a2[..., None] * o2, m, a1 * l1 + a2 * l2
+
+
+def finalize(state):
+    """Normalise: O / l and LSE = m + ln l; a row with l = 0 gives O = 0, LSE = -inf."""
+    o, m, l = (np.asarray(x, dtype=np.float64) for x in state)
+    has = l > 0
+    out = np.zeros_like(o)
+    out[has] = o[has] / l[has][:, None]
+    lse = np.full(m.shape, -np.inf)
+    lse[has] = m[has] + np.log(l[has])
+    return out, lse
+
+
+def ring_emulation(q_local, k_ring, v_ring, q_pos, ring_pos, cp: int, rank: int, causal: bool,
+                   scale=None, order=None, keep_states: bool = False):
+    """One rank's whole ring pass, block by block, in fp64.
+
+    q_local [B, H, Lq, D] with global positions q_pos [Lq]; k_ring/v_ring
+    [B, H, S_pad, D] hold every rank's block rank-major (block s = rows
+    [s*Lk, (s+1)*Lk)), with positions ring_pos [S_pad]. Step t folds the block
+    of rank ``ring_source(rank, t, cp)``; ``order`` overrides the step order
+    (the result must not depend on it beyond rounding).
+    Returns (O, LSE) after finalising, plus the state after each step when
+    ``keep_states``.
+    """
+    q_local = np.asarray(q_local, dtype=np.float64)
+    b_, h_, lq, d = q_local.shape
+    s_pad = np.asarray(k_ring).shape[2]
+    lk = s_pad // cp
+    state = init_state(b_, h_, lq, np.asarray(v_ring).shape[-1])
+    states = []
+    steps = range(cp) if order is None else order
+    for t in steps:
+        src = ring_source(rank, t, cp) if order is None else t
+        sl = slice(src * lk, (src + 1) * lk)
+        state = fold_block(state, q_local, np.asarray(k_ring)[:, :, sl], np.asarray(v_ring)[:, :, sl],
+                           q_pos, np.asarray(ring_pos)[sl], causal, scale)
+        if keep_states:
+            states.append(state)
+    out = finalize(state)
+    return (out, states) if keep_states else out
+
+
+# ---------------------------------------------------------------------------
+# Work counts (the load-balance claim of the Megatron page).
+# ---------------------------------------------------------------------------
+
+def count_pairs(q_pos, k_pos, causal: bool) -> int:
+    """Brute-force number of allowed (query, key) pairs."""
+    return int(allowed_mask(q_pos, k_pos, causal).sum())
+
+
+def causal_pairs_zigzag(s_pad: int, cp: int) -> int:
+    """Allowed causal pairs for one rank under zigzag, with no padding: 2*cp*c^2 + c.
+
+    With c = s_pad/(2*cp): the front chunk r sees r full chunks plus its own
+    triangle, the back chunk 2cp-1-r sees 2cp-1-r full chunks plus its own
+    triangle, so r*c^2 + (2cp-1-r)*c^2 + 2*c(c+1)/2 = 2cp*c^2 + c for any r.
+    """
+    c = s_pad // (2 * cp)
+    return 2 * cp * c * c + c

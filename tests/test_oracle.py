@@ -1,0 +1,370 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each pin ties the oracle to something other than itself: the cp=4 table the
+Megatron page prints, pure-Python brute force on tiny inputs, torch's own
+scaled_dot_product_attention and logsumexp, closed forms, and the pages'
+exactness claim (blockwise ring result == unpartitioned attention). The last
+tests plant mistakes in the oracle (on the CPU) and check that a pin fails.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import ring_attention as ora
+from seeded_inputs import WORKLOADS, gen_tensor, small_workload
+
+ZZ, CT = oracle.ZIGZAG, oracle.CONTIGUOUS
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+# ---------------------------------------------------------------- layout pins
+
+def test_layout_matches_pages_cp4_table(golden_dir):
+    with open(os.path.join(golden_dir, "zigzag_cp4_table.json")) as f:
+        g = json.load(f)
+    cp = g["cp_size"]
+    for c in (1, 3, 5):
+        s = g["n_chunks"] * c
+        tok, pos = oracle.layout(s, cp, ZZ)
+        lr = s // cp
+        for r, (a, b) in enumerate(g["chunks_per_rank"]):
+            local = tok[r * lr:(r + 1) * lr]
+            want = list(range(a * c, a * c + c)) + list(range(b * c, b * c + c))
+            assert local.tolist() == want
+        assert (pos == tok).all()
+
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("s", [1, 7, 16, 33, 64, 100, 257])
+def test_layout_properties(cp, s):
+    for lay in (ZZ, CT):
+        tok, pos = oracle.layout(s, cp, lay)
+        s_pad = len(tok)
+        unit = 2 * cp if lay == ZZ else cp
+        assert s_pad == oracle.padded_len(s, cp, lay)
+        assert s_pad % unit == 0 and s <= s_pad < s + unit
+        assert sorted(tok.tolist()) == list(range(s_pad))          # a permutation
+        assert (pos == np.where(tok < s, tok, -1)).all()            # pads carry -1
+        lr = s_pad // cp
+        for r in range(cp):
+            local = tok[r * lr:(r + 1) * lr]
+            if lay == ZZ:
+                c = lr // 2
+                # two runs of c consecutive tokens: chunk r, then chunk 2cp-1-r
+                assert local[:c].tolist() == list(range(r * c, r * c + c))
+                assert local[c:].tolist() == list(range((2 * cp - 1 - r) * c, (2 * cp - r) * c))
+            else:
+                assert local.tolist() == list(range(r * lr, (r + 1) * lr))
+
+
+def test_padded_len_rejects_bad_args():
+    with pytest.raises(ValueError):
+        oracle.padded_len(10, 0, ZZ)
+    with pytest.raises(ValueError):
+        oracle.padded_len(-1, 2, ZZ)
+    with pytest.raises(ValueError):
+        oracle.padded_len(10, 2, 7)
+
+
+# ------------------------------------------------------- attention definition
+
+def brute_force(q, k, v, qpos, kpos, causal, scale):
+    """Scalar pure-Python softmax attention, one query at a time."""
+    outs, lses = [], []
+    d = len(q[0])
+    for i in range(len(q)):
+        keys = [j for j in range(len(k))
+                if qpos[i] >= 0 and kpos[j] >= 0 and (not causal or kpos[j] <= qpos[i])]
+        if not keys:
+            outs.append([0.0] * len(v[0]))
+            lses.append(-math.inf)
+            continue
+        s = {j: scale * sum(q[i][t] * k[j][t] for t in range(d)) for j in keys}
+        mx = max(s.values())
+        w = {j: math.exp(s[j] - mx) for j in keys}
+        z = sum(w.values())
+        outs.append([sum(w[j] * v[j][t] for j in keys) / z for t in range(len(v[0]))])
+        lses.append(mx + math.log(z))
+    return np.array(outs), np.array(lses)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_full_attention_vs_brute_force(causal, seed):
+    rng = np.random.default_rng(seed)
+    nq, nk, d = 9, 13, 3
+    q, k, v = rnd((1, 1, nq, d), seed), rnd((1, 1, nk, d), seed + 10), rnd((1, 1, nk, d), seed + 20)
+    qpos = rng.permutation(16)[:nq]
+    kpos = rng.permutation(16)[:nk]
+    qpos[2] = -1                      # a pad query
+    kpos[[0, 5]] = -1                 # pad keys
+    scale = 0.7
+    o, lse = oracle.full_attention(q, k, v, qpos, kpos, causal, scale, row_chunk=4)
+    ob, lb = brute_force(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), qpos, kpos, causal, scale)
+    np.testing.assert_allclose(o[0, 0], ob, rtol=0, atol=1e-13)
+    assert np.array_equal(np.isinf(lse[0, 0]), np.isinf(lb))
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(lse[0, 0][fin], lb[fin], rtol=0, atol=1e-13)
+    assert (o[0, 0, 2] == 0).all() and lse[0, 0, 2] == -np.inf
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_attention_vs_torch_sdpa(causal):
+    b, h, s, d = 2, 3, 70, 16
+    q, k, v = rnd((b, h, s, d), 5), rnd((b, h, s, d), 6), rnd((b, h, s, d), 7)
+    pos = np.arange(s)
+    o, lse = oracle.full_attention(q, k, v, pos, pos, causal)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal).numpy()
+    np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+    sc = torch.matmul(tq, tk.transpose(-1, -2)) / math.sqrt(d)
+    if causal:
+        sc = sc.masked_fill(torch.ones(s, s, dtype=torch.bool).triu(1), -math.inf)
+    np.testing.assert_allclose(lse, torch.logsumexp(sc, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_probabilities_sum_to_one():
+    b, h, s, d = 1, 2, 50, 8
+    q, k, v = rnd((b, h, s, d), 8), rnd((b, h, s, d), 9), rnd((b, h, s, d), 10)
+    pos = np.arange(s)
+    _, lse = oracle.full_attention(q, k, v, pos, pos, True)
+    for bb, hh in itertools.product(range(b), range(h)):
+        sc = (q[bb, hh] @ k[bb, hh].T) / math.sqrt(d)
+        p = np.where(np.tril(np.ones((s, s), bool)), np.exp(sc - lse[bb, hh][:, None]), 0.0)
+        np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+
+
+def test_closed_form_zero_keys_gives_prefix_mean():
+    """K = 0: every allowed score is 0, so LSE = ln(#allowed) and O = mean of the allowed V rows."""
+    s, d = 40, 5
+    q, v = rnd((1, 1, s, d), 11), rnd((1, 1, s, d), 12)
+    k = np.zeros((1, 1, s, d))
+    pos = np.arange(s)
+    o, lse = oracle.full_attention(q, k, v, pos, pos, True)
+    np.testing.assert_allclose(lse[0, 0], np.log(np.arange(1, s + 1)), rtol=0, atol=1e-13)
+    prefix_mean = np.cumsum(v[0, 0], axis=0) / np.arange(1, s + 1)[:, None]
+    np.testing.assert_allclose(o[0, 0], prefix_mean, rtol=0, atol=1e-13)
+    o, lse = oracle.full_attention(q, k, v, pos, pos, False)
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(v[0, 0].mean(0), (s, d)), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], math.log(s), rtol=0, atol=1e-13)
+
+
+def test_closed_form_constant_values_and_dominant_key():
+    s, d = 30, 4
+    q, k = rnd((1, 1, s, d), 13), rnd((1, 1, s, d), 14)
+    v = np.full((1, 1, s, d), 2.5)
+    pos = np.arange(s)
+    o, _ = oracle.full_attention(q, k, v, pos, pos, True)
+    np.testing.assert_allclose(o, 2.5, rtol=0, atol=1e-13)
+    # one key whose score dwarfs all others: O is (to fp64) that key's value row
+    k2 = rnd((1, 1, s, d), 15) * 1e-3
+    q2 = np.ones((1, 1, s, d))
+    k2[0, 0, 3] = 400.0
+    v2 = rnd((1, 1, s, d), 16)
+    o2, lse2 = oracle.full_attention(q2, k2, v2, pos, pos, True)
+    np.testing.assert_allclose(o2[0, 0, 3:], np.broadcast_to(v2[0, 0, 3], (s - 3, d)), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse2[0, 0, 3:], 400.0 * d / math.sqrt(d), rtol=0, atol=1e-9)
+
+
+# ------------------------------------------- exactness of the blockwise ring
+
+def ring_inputs(w):
+    q, k, v = (gen_tensor(w, t).astype(np.float64) for t in "qkv")
+    lay = ZZ if w.layout == "zigzag" else CT
+    tok, pos = oracle.layout(w.S, w.cp, lay)
+    s_pad = len(tok)
+
+    def gather(x):
+        out = np.zeros(x.shape[:2] + (s_pad, x.shape[-1]))
+        real = tok < w.S
+        out[:, :, real] = x[:, :, tok[real]]
+        return out
+    return q, k, v, gather(q), gather(k), gather(v), tok, pos, lay
+
+
+@pytest.mark.parametrize("cp", [1, 2, 4, 8])
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ring_emulation_equals_full_attention(cp, layout, causal):
+    w = small_workload("t", "f32", 1, 2, 8, 53, cp, layout, causal, seed=cp * 10 + causal)
+    q, k, v, qr, kr, vr, tok, pos, lay = ring_inputs(w)
+    lr = len(tok) // cp
+    full_o = np.zeros_like(qr)
+    full_l = np.zeros(qr.shape[:3])
+    for r in range(cp):
+        sl = slice(r * lr, (r + 1) * lr)
+        o, lse = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, cp, r, causal)
+        ro, rl = oracle.rank_reference(q, k, v, w.S, cp, lay, r, causal)
+        np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(np.isinf(lse), np.isinf(rl))
+        np.testing.assert_allclose(lse[np.isfinite(rl)], rl[np.isfinite(rl)], rtol=0, atol=1e-12)
+        full_o[:, :, sl], full_l[:, :, sl] = o, lse
+    # reassemble every rank's rows in natural order (inverse layout) == plain attention
+    inv = np.empty(len(tok), np.int64)
+    inv[tok] = np.arange(len(tok))
+    nat = np.arange(w.S)
+    o_nat, l_nat = oracle.full_attention(q, k, v, nat, nat, causal)
+    np.testing.assert_allclose(full_o[:, :, inv[:w.S]], o_nat, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(full_l[:, :, inv[:w.S]], l_nat, rtol=0, atol=1e-12)
+
+
+def test_ring_order_does_not_matter():
+    w = small_workload("t", "f32", 1, 1, 8, 64, 4, "zigzag", True, seed=3)
+    _, _, _, qr, kr, vr, tok, pos, _ = ring_inputs(w)
+    lr = len(tok) // 4
+    r = 1
+    sl = slice(r * lr, (r + 1) * lr)
+    base = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, 4, r, True)
+    for order in ([3, 2, 1, 0], [2, 0, 3, 1]):
+        o, lse = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, 4, r, True, order=order)
+        np.testing.assert_allclose(o, base[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, base[1], rtol=0, atol=1e-12)
+
+
+def test_intermediate_states_equal_attention_over_blocks_seen():
+    """After step t the finalised state equals attention over the t+1 blocks received so far."""
+    w = small_workload("t", "f32", 1, 2, 8, 48, 3, "zigzag", True, seed=4)
+    _, _, _, qr, kr, vr, tok, pos, _ = ring_inputs(w)
+    cp, r = 3, 2
+    lr = len(tok) // cp
+    sl = slice(r * lr, (r + 1) * lr)
+    _, states = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, cp, r, True, keep_states=True)
+    seen = []
+    for t, st in enumerate(states):
+        src = oracle.ring_source(r, t, cp)
+        seen.extend(range(src * lr, (src + 1) * lr))
+        o_ref, l_ref = oracle.full_attention(qr[:, :, sl], kr[:, :, seen], vr[:, :, seen], pos[sl], pos[seen], True)
+        o, lse = oracle.finalize(st)
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(np.isinf(lse), np.isinf(l_ref))
+        fin = np.isfinite(l_ref)
+        np.testing.assert_allclose(lse[fin], l_ref[fin], rtol=0, atol=1e-12)
+
+
+def test_ring_source_is_previous_ranks():
+    assert [oracle.ring_source(0, t, 4) for t in range(4)] == [0, 3, 2, 1]
+    assert [oracle.ring_source(2, t, 4) for t in range(4)] == [2, 1, 0, 3]
+
+
+def test_merge_equals_attention_over_union():
+    b, h, n, d = 1, 2, 12, 6
+    q = rnd((b, h, n, d), 20)
+    k, v = rnd((b, h, 30, d), 21), rnd((b, h, 30, d), 22)
+    qpos = np.arange(10, 22)
+    kpos = np.arange(30)
+    halves = [np.arange(0, 30, 2), np.arange(1, 30, 2)]
+    parts = []
+    for idx in halves:
+        st = oracle.init_state(b, h, n, d)
+        parts.append(oracle.fold_block(st, q, k[:, :, idx], v[:, :, idx], qpos, kpos[idx], True))
+    for a, c in ((0, 1), (1, 0)):
+        o, lse = oracle.finalize(oracle.merge(parts[a], parts[c]))
+        o_ref, l_ref = oracle.full_attention(q, k, v, qpos, kpos, True)
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, l_ref, rtol=0, atol=1e-12)
+    # merging with an empty state is the identity
+    empty = oracle.init_state(b, h, n, d)
+    for x, y in zip(oracle.merge(parts[0], empty), parts[0]):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_fully_masked_rows_mid_ring_stay_finite():
+    q = rnd((1, 1, 4, 3), 30)
+    k, v = rnd((1, 1, 5, 3), 31), rnd((1, 1, 5, 3), 32)
+    st = oracle.init_state(1, 1, 4, 3)
+    st = oracle.fold_block(st, q, k, v, np.array([0, 1, 2, 3]), np.array([10, 11, 12, 13, 14]), True)
+    o, m, l = st
+    assert np.isneginf(m).all() and (l == 0).all() and (o == 0).all()
+    out, lse = oracle.finalize(st)
+    assert (out == 0).all() and np.isneginf(lse).all()
+
+
+# -------------------------------------------------------- work / balance pins
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("c", [1, 2, 5, 8])
+def test_zigzag_balance_closed_form(cp, c):
+    s = 2 * cp * c
+    tok, pos = oracle.layout(s, cp, ZZ)
+    lr = s // cp
+    counts = [oracle.count_pairs(pos[r * lr:(r + 1) * lr], pos, True) for r in range(cp)]
+    assert counts == [oracle.causal_pairs_zigzag(s, cp)] * cp
+    assert sum(counts) == s * (s + 1) // 2
+
+
+def test_contiguous_causal_is_imbalanced():
+    cp, s = 4, 64
+    _, pos = oracle.layout(s, cp, CT)
+    lr = s // cp
+    counts = [oracle.count_pairs(pos[r * lr:(r + 1) * lr], pos, True) for r in range(cp)]
+    assert counts == sorted(counts) and counts[-1] > counts[0]
+
+
+def test_workload_pair_counts():
+    """Closed form at the five workloads' sizes equals a per-chunk count."""
+    for w in WORKLOADS.values():
+        if w.layout != "zigzag":
+            continue
+        c = w.S // (2 * w.cp)
+        for r in w.ranks:
+            chunks = [r, 2 * w.cp - 1 - r]
+            total = 0
+            for qc in chunks:
+                for kc in range(2 * w.cp):
+                    if kc < qc:
+                        total += c * c
+                    elif kc == qc:
+                        total += c * (c + 1) // 2
+            assert total == oracle.causal_pairs_zigzag(w.S, w.cp)
+
+
+# ------------------------------------------------- planted mistakes must fail
+
+def test_planted_strict_mask_is_caught(monkeypatch):
+    def strict(q_pos, k_pos, causal):
+        q_pos = np.asarray(q_pos)[:, None]
+        k_pos = np.asarray(k_pos)[None, :]
+        ok = (q_pos >= 0) & (k_pos >= 0)
+        return ok & (k_pos < q_pos) if causal else ok
+    monkeypatch.setattr(ora, "allowed_mask", strict)
+    s, d = 8, 3
+    q, k, v = rnd((1, 1, s, d), 40), rnd((1, 1, s, d), 41), rnd((1, 1, s, d), 42)
+    pos = np.arange(s)
+    o, _ = ora.full_attention(q, k, v, pos, pos, True)
+    ob, _ = brute_force(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), pos, pos, True, 1 / math.sqrt(d))
+    assert np.abs(o[0, 0] - ob).max() > 1e-3
+
+
+def test_planted_dropped_block_is_caught():
+    w = small_workload("t", "f32", 1, 1, 8, 32, 2, "zigzag", True, seed=5)
+    q, k, v, qr, kr, vr, tok, pos, lay = ring_inputs(w)
+    lr = len(tok) // 2
+    r = 1
+    sl = slice(r * lr, (r + 1) * lr)
+    o, lse = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, 2, r, True, order=[1])
+    ro, rl = oracle.rank_reference(q, k, v, w.S, 2, lay, r, True)
+    assert np.abs(lse - rl).max() > 0.1
+
+
+def test_planted_wrong_chunk_pairing_is_caught(monkeypatch, golden_dir):
+    orig = ora.layout
+
+    def bad_layout(seq_len, cp, lay):
+        tok, pos = orig(seq_len, cp, lay)
+        lr = len(tok) // cp
+        tok = tok.copy()
+        tok[:lr], tok[lr:2 * lr] = tok[lr:2 * lr].copy(), tok[:lr].copy()   # swap two ranks
+        return tok, np.where(tok < seq_len, tok, -1)
+    monkeypatch.setattr(oracle, "layout", bad_layout)
+    with pytest.raises(AssertionError):
+        test_layout_matches_pages_cp4_table(golden_dir)
