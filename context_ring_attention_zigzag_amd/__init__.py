@@ -1,0 +1,171 @@
+"""Python binding of libcpring: per-rank zigzag ring attention on MI355X.
+
+Argument marshalling only. Every step of the computation runs in the HIP
+kernels of ``libcpring.so``; this module turns torch tensors (used as device
+memory) and torch streams into the pointers, strides and sizes the C ABI
+declared in ``include/cpring.h`` expects, and turns non-zero status codes
+into ``CprError``. There is no fallback: if the library is missing, every
+call raises.
+
+Tensors are [B, H, L, D] with the last dimension contiguous; position arrays
+are int32 device tensors.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libcpring.so")
+
+F32, BF16 = 0, 1
+ZIGZAG, CONTIGUOUS = 0, 1
+RUN_FUSED, RUN_STEPWISE = 0, 1
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+
+# Every symbol include/cpring.h declares.
+EXPORTS = (
+    "cp_padded_len", "cp_zigzag_partition", "cp_shard_gather", "cp_ring_attn_init", "cp_ring_attn_step",
+    "cp_ring_attn_merge", "cp_ring_attn_finalize", "cp_ring_attn_workspace_size", "cp_ring_attn_run",
+    "cp_status_string", "cp_last_error",
+)
+
+
+class CprError(RuntimeError):
+    def __init__(self, status: int, func: str, detail: str):
+        super().__init__(f"{func} failed with status {status}: {detail}")
+        self.status = status
+
+
+class CprView(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
+                ("stride_l", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libcpring.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m context_ring_attention_zigzag_amd.build`")
+    lib = ctypes.CDLL(path)
+    i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    pv = ctypes.POINTER(CprView)
+    sig = {
+        "cp_padded_len": (i64, [i64, i32, i32]),
+        "cp_zigzag_partition": (i32, [i64, i32, i32, vp, vp, vp]),
+        "cp_shard_gather": (i32, [i32, i32, i32, i64, i32, pv, vp, i64, vp, vp]),
+        "cp_ring_attn_init": (i32, [i32, i32, i32, i32, vp, vp, vp, vp]),
+        "cp_ring_attn_step": (i32, [i32, i32, i32, i32, pv, i32, vp, pv, pv, i32, vp, i32, f32, vp, vp, vp, vp]),
+        "cp_ring_attn_merge": (i32, [i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]),
+        "cp_ring_attn_finalize": (i32, [i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "cp_ring_attn_workspace_size": (ctypes.c_size_t, [i32, i32, i32, i32]),
+        "cp_ring_attn_run": (i32, [i32, i32, i32, i32, i32, i32, pv, i32, vp, pv, pv, vp, i32, f32, vp, vp, vp,
+                                   ctypes.c_size_t, i32, vp]),
+        "cp_status_string": (ctypes.c_char_p, [i32]),
+        "cp_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, func: str):
+    if status != OK:
+        raise CprError(status, func, load().cp_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def view(t) -> CprView:
+    """cpr_view of a [B, H, L, D] tensor (D must be contiguous)."""
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B, H, L, D] tensor with contiguous last dim")
+    return CprView(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def dtype_code(t) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+# ----------------------------------------------------------------- the ABI
+
+def cp_padded_len(seq_len: int, cp_size: int, layout: int) -> int:
+    return load().cp_padded_len(seq_len, cp_size, layout)
+
+
+def cp_zigzag_partition(seq_len: int, cp_size: int, layout: int, token_idx=None, pos_ids=None, stream=None):
+    _check(load().cp_zigzag_partition(seq_len, cp_size, layout, _ptr(token_idx), _ptr(pos_ids), _stream(stream)),
+           "cp_zigzag_partition")
+
+
+def cp_shard_gather(src, seq_len: int, token_idx, dst, stream=None):
+    B, H, _, D = src.shape
+    v = view(src)
+    _check(load().cp_shard_gather(dtype_code(src), B, H, seq_len, D, ctypes.byref(v), _ptr(token_idx),
+                                  dst.shape[2], _ptr(dst), _stream(stream)), "cp_shard_gather")
+
+
+def cp_ring_attn_init(o_acc, m, l, stream=None):
+    B, H, Lq, D = o_acc.shape
+    _check(load().cp_ring_attn_init(B, H, Lq, D, _ptr(o_acc), _ptr(m), _ptr(l), _stream(stream)),
+           "cp_ring_attn_init")
+
+
+def cp_ring_attn_step(q, q_pos, k, v, kv_pos, causal: bool, softmax_scale: float, o_acc, m, l, stream=None):
+    B, H, Lq, D = q.shape
+    qv, kv, vv = view(q), view(k), view(v)
+    _check(load().cp_ring_attn_step(dtype_code(q), B, H, D, ctypes.byref(qv), Lq, _ptr(q_pos), ctypes.byref(kv),
+                                    ctypes.byref(vv), k.shape[2], _ptr(kv_pos), int(bool(causal)),
+                                    float(softmax_scale), _ptr(o_acc), _ptr(m), _ptr(l), _stream(stream)),
+           "cp_ring_attn_step")
+
+
+def cp_ring_attn_merge(o_acc, m, l, o2, m2, l2, stream=None):
+    B, H, Lq, D = o_acc.shape
+    _check(load().cp_ring_attn_merge(B, H, Lq, D, _ptr(o_acc), _ptr(m), _ptr(l), _ptr(o2), _ptr(m2), _ptr(l2),
+                                     _stream(stream)), "cp_ring_attn_merge")
+
+
+def cp_ring_attn_finalize(o_acc, m, l, o_out, lse_out=None, stream=None):
+    B, H, Lq, D = o_acc.shape
+    _check(load().cp_ring_attn_finalize(dtype_code(o_out), B, H, Lq, D, _ptr(o_acc), _ptr(m), _ptr(l), _ptr(o_out),
+                                        _ptr(lse_out), _stream(stream)), "cp_ring_attn_finalize")
+
+
+def cp_ring_attn_workspace_size(B: int, H: int, Lq: int, D: int) -> int:
+    return load().cp_ring_attn_workspace_size(B, H, Lq, D)
+
+
+def cp_ring_attn_run(q_local, q_pos, k_ring, v_ring, ring_pos, cp_size: int, rank: int, causal: bool,
+                     softmax_scale: float, o_out, lse_out=None, workspace=None, flags: int = RUN_FUSED,
+                     stream=None):
+    B, H, Lq, D = q_local.shape
+    qv, kv, vv = view(q_local), view(k_ring), view(v_ring)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().cp_ring_attn_run(dtype_code(q_local), B, H, D, cp_size, rank, ctypes.byref(qv), Lq, _ptr(q_pos),
+                                   ctypes.byref(kv), ctypes.byref(vv), _ptr(ring_pos), int(bool(causal)),
+                                   float(softmax_scale), _ptr(o_out), _ptr(lse_out), _ptr(workspace), ws_bytes,
+                                   flags, _stream(stream)), "cp_ring_attn_run")

@@ -1,0 +1,291 @@
+// C ABI of libcpring: argument validation and dispatch.
+//
+// Every entry point validates all arguments before it touches the HIP
+// runtime, so a bad call returns an error without launching anything. The
+// library holds no state besides the thread-local text of the last error.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "common.h"
+
+using namespace cpring;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+cpr_status fail(cpr_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+cpr_status ok() {
+  g_last_error.clear();
+  return CPR_OK;
+}
+
+cpr_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(CPR_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int esize_of(int32_t dtype) { return dtype == CPR_BF16 ? 2 : 4; }
+
+// A [B, H, L, D] view with D contiguous.
+cpr_status check_view(const char* name, const cpr_view* v, int32_t dtype) {
+  if (!v) return fail(CPR_EINVAL, "%s: view pointer is NULL", name);
+  if (!v->data) return fail(CPR_EINVAL, "%s: data pointer is NULL", name);
+  if (v->stride_b < 0 || v->stride_h < 0 || v->stride_l < 0)
+    return fail(CPR_EINVAL, "%s: negative stride", name);
+  const int64_t align_elems = dtype == CPR_BF16 ? 8 : 1;   // 16-byte rows for bf16
+  if (dtype == CPR_BF16) {
+    if (!aligned(v->data, 16)) return fail(CPR_EINVAL, "%s: bf16 data must be 16-byte aligned", name);
+    if (v->stride_b % align_elems || v->stride_h % align_elems || v->stride_l % align_elems)
+      return fail(CPR_EINVAL, "%s: bf16 strides must be multiples of 8 elements", name);
+  } else if (!aligned(v->data, 4)) {
+    return fail(CPR_EINVAL, "%s: f32 data must be 4-byte aligned", name);
+  }
+  return CPR_OK;
+}
+
+cpr_status check_dims(int32_t dtype, int32_t B, int32_t H, int32_t D) {
+  if (dtype != CPR_F32 && dtype != CPR_BF16) return fail(CPR_EINVAL, "unknown dtype %d", dtype);
+  if (B < 1 || H < 1) return fail(CPR_EINVAL, "B and H must be >= 1 (got %d, %d)", B, H);
+  if (B > 65535 || H > 65535) return fail(CPR_EUNSUPPORTED, "B and H must be <= 65535");
+  if (D != 64 && D != 128) return fail(CPR_EUNSUPPORTED, "head dim D must be 64 or 128 (got %d)", D);
+  return CPR_OK;
+}
+
+cpr_status check_len(const char* name, int64_t L) {
+  if (L < 1) return fail(CPR_EINVAL, "%s must be >= 1 (got %lld)", name, (long long)L);
+  if (L > CPR_MAX_SEQ) return fail(CPR_EUNSUPPORTED, "%s must be <= 2^30", name);
+  return CPR_OK;
+}
+
+cpr_status check_state(int64_t rows, const float* o, const float* m, const float* l) {
+  if (!o || !m || !l) return fail(CPR_EINVAL, "state pointers o_acc, m, l must be non-NULL");
+  if (!aligned(o, 16)) return fail(CPR_EINVAL, "o_acc must be 16-byte aligned");
+  if (!aligned(m, 4) || !aligned(l, 4)) return fail(CPR_EINVAL, "m and l must be 4-byte aligned");
+  (void)rows;
+  return CPR_OK;
+}
+
+// Grid size of the attention kernels must stay below 2^31 workgroups.
+cpr_status check_grid(int32_t B, int32_t H, int32_t Lq) {
+  const int64_t tiles = (int64_t)B * H * ((Lq + 63) / 64);
+  if (tiles >= ((int64_t)1 << 31)) return fail(CPR_EUNSUPPORTED, "B*H*Lq too large");
+  return CPR_OK;
+}
+
+#define TRY(x)                        \
+  do {                                \
+    cpr_status s__ = (x);             \
+    if (s__ != CPR_OK) return s__;    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int64_t cp_padded_len(int64_t seq_len, int32_t cp_size, int32_t layout) {
+  if (seq_len < 1 || seq_len > CPR_MAX_SEQ || cp_size < 1) return -1;
+  if (layout != CPR_ZIGZAG && layout != CPR_CONTIGUOUS) return -1;
+  const int64_t unit = layout == CPR_ZIGZAG ? 2 * (int64_t)cp_size : (int64_t)cp_size;
+  const int64_t s_pad = (seq_len + unit - 1) / unit * unit;
+  return s_pad > CPR_MAX_SEQ ? -1 : s_pad;
+}
+
+cpr_status cp_zigzag_partition(int64_t seq_len, int32_t cp_size, int32_t layout, int32_t* token_idx,
+                               int32_t* pos_ids, void* stream) {
+  if (cp_size < 1) return fail(CPR_EINVAL, "cp_size must be >= 1 (got %d)", cp_size);
+  if (layout != CPR_ZIGZAG && layout != CPR_CONTIGUOUS) return fail(CPR_EINVAL, "unknown layout %d", layout);
+  TRY(check_len("seq_len", seq_len));
+  const int64_t s_pad = cp_padded_len(seq_len, cp_size, layout);
+  if (s_pad < 0) return fail(CPR_EUNSUPPORTED, "padded length exceeds 2^30");
+  if (!token_idx && !pos_ids) return fail(CPR_EINVAL, "token_idx and pos_ids are both NULL");
+  if ((token_idx && !aligned(token_idx, 4)) || (pos_ids && !aligned(pos_ids, 4)))
+    return fail(CPR_EINVAL, "output arrays must be 4-byte aligned");
+  return hip_status(launch_partition(seq_len, s_pad, cp_size, layout, token_idx, pos_ids,
+                                     static_cast<hipStream_t>(stream)),
+                    "cp_zigzag_partition");
+}
+
+cpr_status cp_shard_gather(int32_t dtype, int32_t B, int32_t H, int64_t seq_len, int32_t D, const cpr_view* src,
+                           const int32_t* token_idx, int64_t n_out, void* dst, void* stream) {
+  TRY(check_dims(dtype, B, H, D));
+  TRY(check_len("seq_len", seq_len));
+  TRY(check_len("n_out", n_out));
+  TRY(check_view("src", src, dtype));
+  if (dtype == CPR_F32) {
+    if (!aligned(src->data, 16) || src->stride_b % 4 || src->stride_h % 4 || src->stride_l % 4)
+      return fail(CPR_EINVAL, "src: f32 gather needs 16-byte aligned rows");
+  }
+  if (!token_idx) return fail(CPR_EINVAL, "token_idx is NULL");
+  if (!dst) return fail(CPR_EINVAL, "dst is NULL");
+  if (!aligned(dst, 16)) return fail(CPR_EINVAL, "dst must be 16-byte aligned");
+  return hip_status(launch_gather(esize_of(dtype), B, H, seq_len, D, *src, token_idx, n_out, dst,
+                                  static_cast<hipStream_t>(stream)),
+                    "cp_shard_gather");
+}
+
+cpr_status cp_ring_attn_init(int32_t B, int32_t H, int32_t Lq, int32_t D, float* o_acc, float* m, float* l,
+                             void* stream) {
+  TRY(check_dims(CPR_F32, B, H, D));
+  TRY(check_len("Lq", Lq));
+  TRY(check_state(0, o_acc, m, l));
+  const int64_t rows = (int64_t)B * H * Lq;
+  return hip_status(launch_state_init(rows, D, o_acc, m, l, static_cast<hipStream_t>(stream)),
+                    "cp_ring_attn_init");
+}
+
+static cpr_status validate_attn(int32_t dtype, int32_t B, int32_t H, int32_t D, const cpr_view* q, int32_t Lq,
+                                const int32_t* q_pos, const cpr_view* k, const cpr_view* v, int64_t Lk_total,
+                                const int32_t* kv_pos) {
+  TRY(check_dims(dtype, B, H, D));
+  TRY(check_len("Lq", Lq));
+  TRY(check_len("KV length", Lk_total));
+  TRY(check_view("q", q, dtype));
+  TRY(check_view("k", k, dtype));
+  TRY(check_view("v", v, dtype));
+  if (!q_pos || !kv_pos) return fail(CPR_EINVAL, "position arrays must be non-NULL");
+  TRY(check_grid(B, H, Lq));
+  return CPR_OK;
+}
+
+static AttnArgs make_args(int32_t dtype, int32_t B, int32_t H, int32_t D, const cpr_view* q, int32_t Lq,
+                          const int32_t* q_pos, const cpr_view* k, const cpr_view* v, int32_t Lk,
+                          const int32_t* kv_pos, int32_t causal, float softmax_scale) {
+  (void)dtype;
+  AttnArgs a{};
+  a.q = q->data; a.q_sb = q->stride_b; a.q_sh = q->stride_h; a.q_sl = q->stride_l;
+  a.q_pos = q_pos;
+  a.k = k->data; a.k_sb = k->stride_b; a.k_sh = k->stride_h; a.k_sl = k->stride_l;
+  a.v = v->data; a.v_sb = v->stride_b; a.v_sh = v->stride_h; a.v_sl = v->stride_l;
+  a.kv_pos = kv_pos;
+  a.B = B; a.H = H; a.D = D; a.Lq = Lq; a.Lk = Lk;
+  a.causal = causal ? 1 : 0;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  return a;
+}
+
+static hipError_t launch_attn(int32_t dtype, const AttnArgs& a, hipStream_t st) {
+  return dtype == CPR_BF16 ? launch_attn_bf16(a, st) : launch_attn_f32(a, st);
+}
+
+cpr_status cp_ring_attn_step(int32_t dtype, int32_t B, int32_t H, int32_t D, const cpr_view* q, int32_t Lq,
+                             const int32_t* q_pos, const cpr_view* k, const cpr_view* v, int32_t Lk,
+                             const int32_t* kv_pos, int32_t causal, float softmax_scale, float* o_acc, float* m,
+                             float* l, void* stream) {
+  TRY(validate_attn(dtype, B, H, D, q, Lq, q_pos, k, v, Lk, kv_pos));
+  TRY(check_state(0, o_acc, m, l));
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
+    return fail(CPR_EINVAL, "softmax_scale must be finite");
+  AttnArgs a = make_args(dtype, B, H, D, q, Lq, q_pos, k, v, Lk, kv_pos, causal, softmax_scale);
+  a.nblocks = 1; a.rank = 0; a.cp = 1;
+  a.o_acc = o_acc; a.m = m; a.l = l;
+  a.load_state = 1; a.finalize = 0;
+  return hip_status(launch_attn(dtype, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_step");
+}
+
+cpr_status cp_ring_attn_merge(int32_t B, int32_t H, int32_t Lq, int32_t D, float* o_acc, float* m, float* l,
+                              const float* o2, const float* m2, const float* l2, void* stream) {
+  TRY(check_dims(CPR_F32, B, H, D));
+  TRY(check_len("Lq", Lq));
+  TRY(check_state(0, o_acc, m, l));
+  if (!o2 || !m2 || !l2) return fail(CPR_EINVAL, "partial-state pointers must be non-NULL");
+  if (!aligned(o2, 16) || !aligned(m2, 4) || !aligned(l2, 4)) return fail(CPR_EINVAL, "o2 must be 16-byte aligned");
+  const int64_t rows = (int64_t)B * H * Lq;
+  return hip_status(launch_merge(rows, D, o_acc, m, l, o2, m2, l2, static_cast<hipStream_t>(stream)),
+                    "cp_ring_attn_merge");
+}
+
+cpr_status cp_ring_attn_finalize(int32_t out_dtype, int32_t B, int32_t H, int32_t Lq, int32_t D,
+                                 const float* o_acc, const float* m, const float* l, void* o_out, float* lse_out,
+                                 void* stream) {
+  TRY(check_dims(out_dtype, B, H, D));
+  TRY(check_len("Lq", Lq));
+  TRY(check_state(0, o_acc, m, l));
+  if (!o_out) return fail(CPR_EINVAL, "o_out is NULL");
+  if (!aligned(o_out, 16)) return fail(CPR_EINVAL, "o_out must be 16-byte aligned");
+  if (lse_out && !aligned(lse_out, 4)) return fail(CPR_EINVAL, "lse_out must be 4-byte aligned");
+  const int64_t rows = (int64_t)B * H * Lq;
+  return hip_status(launch_finalize(out_dtype == CPR_BF16, rows, D, o_acc, m, l, o_out, lse_out,
+                                    static_cast<hipStream_t>(stream)),
+                    "cp_ring_attn_finalize");
+}
+
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t cp_ring_attn_workspace_size(int32_t B, int32_t H, int32_t Lq, int32_t D) {
+  if (B < 1 || H < 1 || Lq < 1 || (D != 64 && D != 128)) return 0;
+  const size_t rows = (size_t)B * H * Lq;
+  return round256(rows * D * sizeof(float)) + 2 * round256(rows * sizeof(float));
+}
+
+cpr_status cp_ring_attn_run(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t cp_size, int32_t rank,
+                            const cpr_view* q_local, int32_t Lq, const int32_t* q_pos, const cpr_view* k_ring,
+                            const cpr_view* v_ring, const int32_t* ring_pos, int32_t causal, float softmax_scale,
+                            void* o_out, float* lse_out, void* workspace, size_t workspace_bytes, int32_t flags,
+                            void* stream) {
+  if (cp_size < 1) return fail(CPR_EINVAL, "cp_size must be >= 1 (got %d)", cp_size);
+  if (rank < 0 || rank >= cp_size) return fail(CPR_EINVAL, "rank %d outside [0, %d)", rank, cp_size);
+  TRY(validate_attn(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, (int64_t)Lq * cp_size, ring_pos));
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
+    return fail(CPR_EINVAL, "softmax_scale must be finite");
+  if (!o_out) return fail(CPR_EINVAL, "o_out is NULL");
+  if (!aligned(o_out, 16)) return fail(CPR_EINVAL, "o_out must be 16-byte aligned");
+  if (lse_out && !aligned(lse_out, 4)) return fail(CPR_EINVAL, "lse_out must be 4-byte aligned");
+  if (flags != CPR_RUN_FUSED && flags != CPR_RUN_STEPWISE) return fail(CPR_EINVAL, "unknown flags %d", flags);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  AttnArgs a = make_args(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, Lq, ring_pos, causal, softmax_scale);
+  if (flags == CPR_RUN_FUSED) {
+    a.nblocks = cp_size; a.rank = rank; a.cp = cp_size;
+    a.o_out = o_out; a.lse = lse_out;
+    a.load_state = 0; a.finalize = 1;
+    return hip_status(launch_attn(dtype, a, st), "cp_ring_attn_run");
+  }
+  const size_t need = cp_ring_attn_workspace_size(B, H, Lq, D);
+  if (!workspace || workspace_bytes < need)
+    return fail(CPR_EINVAL, "stepwise run needs a workspace of %zu bytes", need);
+  if (!aligned(workspace, 256)) return fail(CPR_EINVAL, "workspace must be 256-byte aligned");
+  const size_t rows = (size_t)B * H * Lq;
+  char* w = static_cast<char*>(workspace);
+  float* o_acc = reinterpret_cast<float*>(w);
+  float* m = reinterpret_cast<float*>(w + round256(rows * D * sizeof(float)));
+  float* l = reinterpret_cast<float*>(w + round256(rows * D * sizeof(float)) + round256(rows * sizeof(float)));
+  hipError_t e = launch_state_init((int64_t)rows, D, o_acc, m, l, st);
+  if (e != hipSuccess) return hip_status(e, "cp_ring_attn_run(init)");
+  a.o_acc = o_acc; a.m = m; a.l = l;
+  a.load_state = 1; a.finalize = 0; a.nblocks = 1; a.cp = cp_size;
+  for (int t = 0; t < cp_size; ++t) {
+    a.rank = ((rank - t) % cp_size + cp_size) % cp_size;   // block held after t hops
+    e = launch_attn(dtype, a, st);
+    if (e != hipSuccess) return hip_status(e, "cp_ring_attn_run(step)");
+  }
+  return hip_status(launch_finalize(dtype == CPR_BF16, (int64_t)rows, D, o_acc, m, l, o_out, lse_out, st),
+                    "cp_ring_attn_run(finalize)");
+}
+
+const char* cp_status_string(int32_t status) {
+  switch (status) {
+    case CPR_OK: return "ok";
+    case CPR_EINVAL: return "invalid argument";
+    case CPR_EUNSUPPORTED: return "unsupported configuration";
+    case CPR_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* cp_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,44 @@
+// Internal declarations shared by the libcpring translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cpring.h"
+
+namespace cpring {
+
+// Kernel launchers; each returns hipSuccess or the launch error.
+hipError_t launch_partition(int64_t seq_len, int64_t s_pad, int32_t cp, int32_t layout,
+                            int32_t* token_idx, int32_t* pos_ids, hipStream_t st);
+hipError_t launch_gather(int esize, int32_t B, int32_t H, int64_t seq_len, int32_t D, const cpr_view& src,
+                         const int32_t* token_idx, int64_t n_out, void* dst, hipStream_t st);
+hipError_t launch_state_init(int64_t rows, int32_t D, float* o, float* m, float* l, hipStream_t st);
+hipError_t launch_merge(int64_t rows, int32_t D, float* o, float* m, float* l, const float* o2,
+                        const float* m2, const float* l2, hipStream_t st);
+hipError_t launch_finalize(int out_bf16, int64_t rows, int32_t D, const float* o, const float* m,
+                           const float* l, void* out, float* lse, hipStream_t st);
+
+// Attention pass over `nblocks` KV blocks of Lk rows. Block t (t = 0..nblocks-1)
+// is block (rank - t) mod cp of the K/V/kv_pos buffers. State handling:
+// load_state reads (o_acc, m, l) first (else starts from O=0, m=-inf, l=0);
+// finalize writes (o_out, lse) at the end (else writes (o_acc, m, l) back).
+struct AttnArgs {
+  const void* q; int64_t q_sb, q_sh, q_sl;
+  const int32_t* q_pos;
+  const void* k; int64_t k_sb, k_sh, k_sl;
+  const void* v; int64_t v_sb, v_sh, v_sl;
+  const int32_t* kv_pos;
+  int32_t B, H, D, Lq, Lk;
+  int32_t nblocks, rank, cp;
+  int32_t causal;
+  float scale;
+  float* o_acc; float* m; float* l;
+  void* o_out; float* lse;
+  int32_t load_state, finalize;
+};
+
+hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
+
+}  // namespace cpring

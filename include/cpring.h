@@ -1,0 +1,206 @@
+/*
+ * cpring.h - C ABI of libcpring: one context-parallel rank's ring-attention
+ * forward pass, for AMD Instinct MI355X (gfx950).
+ *
+ * Method (pages cited by title and section):
+ *  - "Context Parallelism" (Ultralytics glossary), "How context parallelism
+ *    works": each device computes partial attention on its local data, hands
+ *    its KV block to the next device, and repeats until the whole sequence is
+ *    seen; the result equals full-sequence attention up to rounding.
+ *  - "Sequence Parallelism and Ring Attention" (aiunderstanding.org), "Deep
+ *    dive" and "Technical insight": local queries stay put while KV blocks
+ *    travel the ring; each arriving block is folded in with the online-softmax
+ *    running max / running sum, rescaling earlier partial sums when a larger
+ *    score appears.
+ *  - "Context Parallelism v.s. Sequence Parallelism (Megatron-LM)",
+ *    "Implementation quirk: symmetric chunk assignment": the sequence is cut
+ *    into 2*cp chunks and rank r holds chunks r and 2*cp-1-r, so every rank
+ *    does the same causal work; positions and masks must use global token
+ *    positions; the sequence is padded to a multiple of 2*cp.
+ *
+ * Conventions shared by every call:
+ *  - Tensors are [B, H, L, D] (sequence on dim 2, as in the SDPA call on the
+ *    glossary page, "Practical use and trade-offs"). A cpr_view gives element
+ *    strides for B, H and L; the D dimension must be contiguous. Views of
+ *    bf16 tensors need every stride and the base address 16-byte aligned.
+ *  - Every pointer argument named as device memory must point to memory of
+ *    the current HIP device; position arrays are int32 device arrays.
+ *  - The caller owns every buffer. The library never allocates or frees
+ *    device memory and keeps no state between calls.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream) and does not synchronise. Results are valid once the stream has
+ *    reached the call.
+ *  - Arguments are validated before anything is launched. On failure the call
+ *    returns a non-zero cpr_status, launches nothing, and cp_last_error()
+ *    describes the problem. A launch failure returns CPR_EHIP. No C++
+ *    exception crosses this boundary. Results are deterministic: no atomics
+ *    are used, so the same inputs give bit-identical outputs.
+ *  - The state of a rank between ring steps is (O, m, l), all float32 and
+ *    contiguous: O [B, H, Lq, D] is the unnormalised output
+ *    sum_j exp(s_j - m) v_j, m [B, H, Lq] the running max of the allowed
+ *    scaled scores s (natural-log units, -inf when nothing was allowed yet),
+ *    l [B, H, Lq] the running sum_j exp(s_j - m).
+ *  - A key j is allowed for query i iff pos_j >= 0, pos_i >= 0 and, when
+ *    causal, pos_j <= pos_i (global positions; -1 marks a pad token). A query
+ *    with no allowed key finalises to O = 0, LSE = -inf.
+ *  - softmax_scale <= 0 selects 1/sqrt(D), the SDPA default.
+ *  - Values in pad rows of K and V must be finite (zero-filled rows, as
+ *    cp_shard_gather writes, are fine): they are multiplied by zero weights.
+ */
+#ifndef CPRING_H
+#define CPRING_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CPR_OK = 0,
+  CPR_EINVAL = 1,       /* an argument is out of range, null or misaligned */
+  CPR_EUNSUPPORTED = 2, /* valid request outside what the kernels implement */
+  CPR_EHIP = 3          /* the HIP runtime reported an error at launch */
+} cpr_status;
+
+typedef enum { CPR_F32 = 0, CPR_BF16 = 1 } cpr_dtype;
+
+typedef enum {
+  CPR_ZIGZAG = 0,     /* rank r: chunks r and 2cp-1-r of 2cp chunks */
+  CPR_CONTIGUOUS = 1  /* rank r: tokens [r*L/cp, (r+1)*L/cp) */
+} cpr_layout;
+
+/* Flags for cp_ring_attn_run. */
+enum {
+  CPR_RUN_FUSED = 0,    /* one launch walks every ring block; no workspace */
+  CPR_RUN_STEPWISE = 1  /* init, cp calls of the step kernel, finalize; needs the workspace */
+};
+
+/* Strided [B, H, L, D] view; strides in elements, D contiguous. */
+typedef struct cpr_view {
+  const void* data;
+  int64_t stride_b;
+  int64_t stride_h;
+  int64_t stride_l;
+} cpr_view;
+
+/* Largest supported values. */
+#define CPR_MAX_SEQ ((int64_t)1 << 30)
+
+/*
+ * Padded sequence length for `seq_len` tokens over `cp_size` ranks: the next
+ * multiple of 2*cp_size for CPR_ZIGZAG (Megatron page, symmetric chunk
+ * assignment: the sequence must split into 2*cp equal chunks), of cp_size for
+ * CPR_CONTIGUOUS ("Sequence Parallelism and Ring Attention", "Deep dive").
+ * Returns -1 for seq_len < 1 or > CPR_MAX_SEQ, cp_size < 1, or an unknown layout.
+ */
+int64_t cp_padded_len(int64_t seq_len, int32_t cp_size, int32_t layout);
+
+/*
+ * Token and position-id layout of all ranks, rank-major: entry r*Lr + i
+ * (Lr = S_pad/cp_size) describes the i-th local token of rank r.
+ *   token_idx[k]  index of that token in the padded natural order
+ *                 (zigzag: chunk r then chunk 2cp-1-r, each in order);
+ *   pos_ids[k]    its global position, or -1 for a pad token (>= seq_len).
+ * Both are int32 device arrays of cp_padded_len(...) entries; either may be
+ * NULL (not both). Cited: Megatron page, symmetric chunk assignment (chunk
+ * pairing, global positions for position ids and masks, padding).
+ */
+cpr_status cp_zigzag_partition(int64_t seq_len, int32_t cp_size, int32_t layout,
+                               int32_t* token_idx, int32_t* pos_ids, void* stream);
+
+/*
+ * Gather rows into layout order: dst[b,h,i,:] = src[b,h,token_idx[i],:] when
+ * 0 <= token_idx[i] < seq_len, else zeros (pad rows). dst is a contiguous
+ * [B, H, n_out, D] device buffer of `dtype`; src a view of [B, H, seq_len, D].
+ * This materialises a rank's local Q (token_idx of that rank) or the
+ * ring-ordered K and V of all ranks (the whole token_idx), the inputs that the
+ * Megatron page says must follow the chunk pairing.
+ */
+cpr_status cp_shard_gather(int32_t dtype, int32_t B, int32_t H, int64_t seq_len, int32_t D,
+                           const cpr_view* src, const int32_t* token_idx, int64_t n_out,
+                           void* dst, void* stream);
+
+/*
+ * Reset the running state before the first ring step: O = 0, m = -inf, l = 0
+ * ("Sequence Parallelism and Ring Attention", "Technical insight").
+ * o_acc [B,H,Lq,D], m and l [B,H,Lq]: contiguous float32 device buffers.
+ */
+cpr_status cp_ring_attn_init(int32_t B, int32_t H, int32_t Lq, int32_t D,
+                             float* o_acc, float* m, float* l, void* stream);
+
+/*
+ * One ring step: fold the KV block that has just arrived into the running
+ * state of the local queries ("Sequence Parallelism and Ring Attention",
+ * "Deep dive": blockwise attention with the running max/sum trick).
+ *   q        [B,H,Lq,D] local queries, with global positions q_pos [Lq];
+ *   k, v     [B,H,Lk,D] one KV block, with global positions kv_pos [Lk];
+ *   causal   non-zero: key allowed only if kv_pos <= q_pos;
+ *   o_acc, m, l  the state (see above), read and updated in place.
+ * dtype CPR_BF16 runs on bf16 MFMA with float32 accumulation (the
+ * probabilities are rounded to bf16 before the P*V product); CPR_F32 runs in
+ * float32. D must be 64 or 128. q/k/v must not alias the state.
+ */
+cpr_status cp_ring_attn_step(int32_t dtype, int32_t B, int32_t H, int32_t D,
+                             const cpr_view* q, int32_t Lq, const int32_t* q_pos,
+                             const cpr_view* k, const cpr_view* v, int32_t Lk, const int32_t* kv_pos,
+                             int32_t causal, float softmax_scale,
+                             float* o_acc, float* m, float* l, void* stream);
+
+/*
+ * Fold a second partial state (o2, m2, l2), built over a disjoint set of keys,
+ * into (o_acc, m, l) in place: m' = max(m, m2), each side scaled by
+ * exp(m_side - m') (the same rescaling rule, "Technical insight").
+ * All buffers contiguous float32, shapes as for the state.
+ */
+cpr_status cp_ring_attn_merge(int32_t B, int32_t H, int32_t Lq, int32_t D,
+                              float* o_acc, float* m, float* l,
+                              const float* o2, const float* m2, const float* l2, void* stream);
+
+/*
+ * Normalise the state after the last step: o_out = O / l, rounded to nearest
+ * even in out_dtype (CPR_BF16 or CPR_F32), and lse_out = m + ln l (float32).
+ * Rows with l = 0 give O = 0, LSE = -inf. o_out is a contiguous [B,H,Lq,D]
+ * device buffer, lse_out a contiguous [B,H,Lq] float32 buffer (may be NULL).
+ */
+cpr_status cp_ring_attn_finalize(int32_t out_dtype, int32_t B, int32_t H, int32_t Lq, int32_t D,
+                                 const float* o_acc, const float* m, const float* l,
+                                 void* o_out, float* lse_out, void* stream);
+
+/* Workspace bytes cp_ring_attn_run needs with CPR_RUN_STEPWISE (the float32
+ * state); CPR_RUN_FUSED needs none. Returns 0 for invalid sizes. */
+size_t cp_ring_attn_workspace_size(int32_t B, int32_t H, int32_t Lq, int32_t D);
+
+/*
+ * One rank's whole ring pass: Lq = Lk local tokens per rank, cp_size blocks.
+ *   q_local  [B,H,Lq,D] the rank's queries, positions q_pos [Lq];
+ *   k_ring, v_ring  [B,H,cp_size*Lq,D] every rank's KV block, rank-major
+ *            (block s = rows [s*Lq, (s+1)*Lq)), positions ring_pos [cp_size*Lq];
+ *   rank     0 <= rank < cp_size.
+ * Step t folds the block of rank (rank - t) mod cp_size: after t hops of a
+ * ring in which every device passes its block to the next, that is the block
+ * rank `rank` holds ("Context Parallelism", "How context parallelism works").
+ * Writes o_out [B,H,Lq,D] (dtype, contiguous) and lse_out [B,H,Lq] (float32,
+ * may be NULL). flags: CPR_RUN_FUSED or CPR_RUN_STEPWISE; the latter needs
+ * `workspace` of cp_ring_attn_workspace_size() bytes (256-byte aligned).
+ */
+cpr_status cp_ring_attn_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
+                            int32_t cp_size, int32_t rank,
+                            const cpr_view* q_local, int32_t Lq, const int32_t* q_pos,
+                            const cpr_view* k_ring, const cpr_view* v_ring, const int32_t* ring_pos,
+                            int32_t causal, float softmax_scale,
+                            void* o_out, float* lse_out,
+                            void* workspace, size_t workspace_bytes, int32_t flags, void* stream);
+
+/* Static description of a status code. */
+const char* cp_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* cp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPRING_H */

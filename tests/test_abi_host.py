@@ -1,0 +1,188 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/cpring.h declares, and
+reject bad arguments before it touches the HIP runtime. Only argument
+validation runs here: every call below fails validation, so nothing is
+launched.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import context_ring_attention_zigzag_amd as cpr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpring.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(cpr.LIB_PATH):
+        from context_ring_attention_zigzag_amd import build
+        build.build()
+    return cpr.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(cpr.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", cpr.LIB_PATH], capture_output=True, text=True, check=True)
+    exported = {line.split()[-1] for line in out.stdout.splitlines() if line.strip()}
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_padded_len(lib):
+    assert lib.cp_padded_len(4096, 2, cpr.ZIGZAG) == 4096
+    assert lib.cp_padded_len(4097, 2, cpr.ZIGZAG) == 4100
+    assert lib.cp_padded_len(1, 4, cpr.ZIGZAG) == 8
+    assert lib.cp_padded_len(65536, 8, cpr.CONTIGUOUS) == 65536
+    assert lib.cp_padded_len(10, 4, cpr.CONTIGUOUS) == 12
+    assert lib.cp_padded_len(1048576, 8, cpr.ZIGZAG) == 1048576
+    for bad in ((0, 2, 0), (-5, 2, 0), (10, 0, 0), (10, 2, 5), (1 << 31, 2, 0)):
+        assert lib.cp_padded_len(*bad) == -1
+
+
+def test_padded_len_matches_oracle(lib):
+    import oracle
+    for s in (1, 3, 17, 64, 100, 257, 4096):
+        for cp in (1, 2, 3, 4, 8):
+            for lay in (cpr.ZIGZAG, cpr.CONTIGUOUS):
+                assert lib.cp_padded_len(s, cp, lay) == oracle.padded_len(s, cp, lay)
+
+
+def fake_ptr(n=0x100000):
+    return ctypes.c_void_p(n)
+
+
+def view(ptr=0x100000, sb=0, sh=0, sl=128):
+    return cpr.CprView(ptr, sb, sh, sl)
+
+
+def err(lib):
+    return lib.cp_last_error().decode()
+
+
+def test_status_strings(lib):
+    for s in (0, 1, 2, 3, 99):
+        assert lib.cp_status_string(s)
+
+
+def test_partition_validation(lib):
+    p = fake_ptr()
+    assert lib.cp_zigzag_partition(100, 0, cpr.ZIGZAG, p, p, None) == cpr.EINVAL
+    assert "cp_size" in err(lib)
+    assert lib.cp_zigzag_partition(100, 2, 9, p, p, None) == cpr.EINVAL
+    assert lib.cp_zigzag_partition(0, 2, cpr.ZIGZAG, p, p, None) == cpr.EINVAL
+    assert lib.cp_zigzag_partition(100, 2, cpr.ZIGZAG, None, None, None) == cpr.EINVAL
+    assert lib.cp_zigzag_partition(100, 2, cpr.ZIGZAG, ctypes.c_void_p(0x100002), None, None) == cpr.EINVAL
+    assert lib.cp_zigzag_partition(1 << 31, 2, cpr.ZIGZAG, p, p, None) == cpr.EUNSUPPORTED
+
+
+def step_args(**over):
+    a = dict(dtype=cpr.BF16, B=1, H=2, D=128, q=view(), Lq=64, q_pos=fake_ptr(), k=view(), v=view(), Lk=64,
+             kv_pos=fake_ptr(), causal=1, scale=0.0, o=fake_ptr(), m=fake_ptr(), l=fake_ptr())
+    a.update(over)
+    return a
+
+
+def call_step(lib, a):
+    return lib.cp_ring_attn_step(a["dtype"], a["B"], a["H"], a["D"], ctypes.byref(a["q"]) if a["q"] else None,
+                                 a["Lq"], a["q_pos"], ctypes.byref(a["k"]) if a["k"] else None,
+                                 ctypes.byref(a["v"]) if a["v"] else None, a["Lk"], a["kv_pos"], a["causal"],
+                                 a["scale"], a["o"], a["m"], a["l"], None)
+
+
+@pytest.mark.parametrize("over,code,needle", [
+    (dict(dtype=7), cpr.EINVAL, "dtype"),
+    (dict(D=96), cpr.EUNSUPPORTED, "head dim"),
+    (dict(D=256), cpr.EUNSUPPORTED, "head dim"),
+    (dict(B=0), cpr.EINVAL, "B and H"),
+    (dict(H=-1), cpr.EINVAL, "B and H"),
+    (dict(Lq=0), cpr.EINVAL, "Lq"),
+    (dict(Lk=0), cpr.EINVAL, "KV length"),
+    (dict(q=None), cpr.EINVAL, "q"),
+    (dict(q=view(ptr=0)), cpr.EINVAL, "q: data pointer"),
+    (dict(k=view(ptr=0x100008)), cpr.EINVAL, "16-byte aligned"),
+    (dict(v=view(sl=100)), cpr.EINVAL, "multiples of 8"),
+    (dict(v=view(sb=-8)), cpr.EINVAL, "negative stride"),
+    (dict(q_pos=None), cpr.EINVAL, "position"),
+    (dict(kv_pos=None), cpr.EINVAL, "position"),
+    (dict(o=None), cpr.EINVAL, "state"),
+    (dict(o=fake_ptr(0x100004)), cpr.EINVAL, "o_acc"),
+    (dict(scale=float("nan")), cpr.EINVAL, "softmax_scale"),
+    (dict(scale=float("inf")), cpr.EINVAL, "softmax_scale"),
+])
+def test_step_validation(lib, over, code, needle):
+    assert call_step(lib, step_args(**over)) == code
+    assert needle in err(lib)
+
+
+def call_run(lib, cp=2, rank=0, flags=cpr.RUN_FUSED, ws=None, ws_bytes=0, out=fake_ptr(), dtype=cpr.BF16, D=128,
+             Lq=64):
+    q, k, v = view(), view(), view()
+    return lib.cp_ring_attn_run(dtype, 1, 2, D, cp, rank, ctypes.byref(q), Lq, fake_ptr(), ctypes.byref(k),
+                                ctypes.byref(v), fake_ptr(), 1, 0.0, out, None, ws, ws_bytes, flags, None)
+
+
+def test_run_validation(lib):
+    assert call_run(lib, cp=0) == cpr.EINVAL
+    assert call_run(lib, cp=4, rank=4) == cpr.EINVAL and "rank" in err(lib)
+    assert call_run(lib, rank=-1) == cpr.EINVAL
+    assert call_run(lib, flags=5) == cpr.EINVAL and "flags" in err(lib)
+    assert call_run(lib, out=None) == cpr.EINVAL and "o_out" in err(lib)
+    assert call_run(lib, flags=cpr.RUN_STEPWISE) == cpr.EINVAL and "workspace" in err(lib)
+    need = lib.cp_ring_attn_workspace_size(1, 2, 64, 128)
+    assert call_run(lib, flags=cpr.RUN_STEPWISE, ws=fake_ptr(), ws_bytes=need - 1) == cpr.EINVAL
+    assert call_run(lib, flags=cpr.RUN_STEPWISE, ws=fake_ptr(0x100010), ws_bytes=need) == cpr.EINVAL
+    assert "256-byte" in err(lib)
+    assert call_run(lib, D=32) == cpr.EUNSUPPORTED
+    assert call_run(lib, Lq=(1 << 30), cp=2) == cpr.EUNSUPPORTED
+
+
+def test_workspace_size(lib):
+    ws = lib.cp_ring_attn_workspace_size(2, 16, 8192, 128)
+    rows = 2 * 16 * 8192
+    assert ws >= rows * 128 * 4 + 2 * rows * 4 and ws % 256 == 0
+    assert lib.cp_ring_attn_workspace_size(0, 1, 1, 128) == 0
+    assert lib.cp_ring_attn_workspace_size(1, 1, 1, 100) == 0
+
+
+def test_state_call_validation(lib):
+    p = fake_ptr()
+    assert lib.cp_ring_attn_init(1, 1, 0, 128, p, p, p, None) == cpr.EINVAL
+    assert lib.cp_ring_attn_init(1, 1, 8, 128, None, p, p, None) == cpr.EINVAL
+    assert lib.cp_ring_attn_merge(1, 1, 8, 128, p, p, p, None, p, p, None) == cpr.EINVAL
+    assert lib.cp_ring_attn_merge(1, 1, 8, 100, p, p, p, p, p, p, None) == cpr.EUNSUPPORTED
+    assert lib.cp_ring_attn_finalize(cpr.BF16, 1, 1, 8, 128, p, p, p, None, None, None) == cpr.EINVAL
+    assert lib.cp_ring_attn_finalize(5, 1, 1, 8, 128, p, p, p, p, None, None) == cpr.EINVAL
+    assert lib.cp_ring_attn_finalize(cpr.F32, 1, 1, 8, 128, p, p, p, fake_ptr(0x100008), None, None) == cpr.EINVAL
+
+
+def test_gather_validation(lib):
+    v = view()
+    p = fake_ptr()
+    assert lib.cp_shard_gather(cpr.BF16, 1, 1, 100, 128, ctypes.byref(v), None, 10, p, None) == cpr.EINVAL
+    assert lib.cp_shard_gather(cpr.BF16, 1, 1, 100, 128, ctypes.byref(v), p, 10, None, None) == cpr.EINVAL
+    assert lib.cp_shard_gather(cpr.BF16, 1, 1, 100, 128, ctypes.byref(v), p, 0, p, None) == cpr.EINVAL
+    bad = view(sl=130)
+    assert lib.cp_shard_gather(cpr.F32, 1, 1, 100, 128, ctypes.byref(bad), p, 10, p, None) == cpr.EINVAL
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(cpr, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        cpr.load(str(tmp_path / "nope.so"))

@@ -1,0 +1,363 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars: layout and gather outputs bit-exact; bf16 inputs O max-abs <= 2e-2 and
+LSE max-abs <= 1e-3; float32 inputs <= 1e-5 on both. Small cases compare
+every row; the 32k / 64k / 1M-token workloads compare sampled rows (first and
+last rows of every local chunk plus seeded rows) in the launch configuration
+the benchmark times, and the 1M-token share is also checked on every row
+against the K = 0 closed form (LSE = ln #allowed, O = mean of allowed V).
+"""
+
+import math
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import context_ring_attention_zigzag_amd as cpr
+from context_ring_attention_zigzag_amd import device_inputs as di
+from seeded_inputs import WORKLOADS, gen_slice, sample_rows, small_workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": (2e-2, 1e-3), "f32": (1e-5, 1e-5)}
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cpr.load()
+    yield
+
+
+def note(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+
+
+def lay_code(w):
+    return cpr.ZIGZAG if w.layout == "zigzag" else cpr.CONTIGUOUS
+
+
+def compare(o, lse, ro, rl, dtype, what):
+    tol_o, tol_l = TOL[dtype]
+    assert np.array_equal(np.isneginf(lse), np.isneginf(rl)), f"{what}: -inf LSE pattern differs"
+    fin = np.isfinite(rl)
+    err_l = float(np.abs(lse[fin] - rl[fin]).max()) if fin.any() else 0.0
+    err_o = float(np.abs(o - ro).max())
+    note(f"{what}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}")
+    assert np.isfinite(o).all()
+    assert err_o <= tol_o, f"{what}: O error {err_o} > {tol_o}"
+    assert err_l <= tol_l, f"{what}: LSE error {err_l} > {tol_l}"
+
+
+def natural_inputs(w):
+    """GPU natural-order tensors and the float64 host copies of the same values."""
+    host = {t: np.stack([np.stack([gen_slice(w, t, b, h) for h in range(w.H)]) for b in range(w.B)])
+            for t in "qkv"}
+    dev = {t: torch.from_numpy(host[t]).to(TDT[w.dtype]).cuda() for t in "qkv"}
+    return dev, {t: host[t].astype(np.float64) for t in "qkv"}
+
+
+def run_rank(w, dev, rank, flags):
+    ri = di.prepare_rank(dev["q"], dev["k"], dev["v"], w.S, w.cp, lay_code(w), rank)
+    o = torch.empty_like(ri.q_local)
+    lse = torch.empty(ri.q_local.shape[:3], dtype=torch.float32, device="cuda")
+    ws = None
+    if flags == cpr.RUN_STEPWISE:
+        ws = torch.empty(cpr.cp_ring_attn_workspace_size(w.B, w.H, ri.lq, w.D), dtype=torch.uint8, device="cuda")
+    cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, w.causal, 0.0, o, lse,
+                         ws, flags)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy(), ri
+
+
+# --------------------------------------------------------------- layout
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("s", [1, 5, 64, 100, 257, 4096, 32768])
+def test_partition_bit_exact(cp, s):
+    for lay in (cpr.ZIGZAG, cpr.CONTIGUOUS):
+        tok, pos = di.layout_arrays(s, cp, lay)
+        rt, rp = oracle.layout(s, cp, lay)
+        assert np.array_equal(tok.cpu().numpy(), rt.astype(np.int32))
+        assert np.array_equal(pos.cpu().numpy(), rp.astype(np.int32))
+
+
+def test_partition_million_tokens_bit_exact():
+    w = WORKLOADS["million_cp8"]
+    tok, pos = di.layout_arrays(w.S, w.cp, cpr.ZIGZAG)
+    rt, rp = oracle.layout(w.S, w.cp, oracle.ZIGZAG)
+    assert np.array_equal(tok.cpu().numpy(), rt.astype(np.int32))
+    assert np.array_equal(pos.cpu().numpy(), rp.astype(np.int32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gather_bit_exact(dtype):
+    B, H, S, D = 2, 3, 77, 128
+    x = torch.randn(B, H, S, D).to(TDT[dtype])
+    tok, _ = di.layout_arrays(S, 4, cpr.ZIGZAG)
+    out = di.gather(x.cuda(), S, tok)
+    t = tok.cpu().numpy().astype(np.int64)
+    ref = torch.zeros(B, H, len(t), D, dtype=TDT[dtype])
+    real = t < S
+    ref[:, :, torch.from_numpy(np.nonzero(real)[0])] = x[:, :, torch.from_numpy(t[real])]
+    assert torch.equal(out.cpu(), ref)
+    # strided source view (every other head of a larger tensor)
+    big = torch.randn(B, 2 * H, S, D).to(TDT[dtype]).cuda()
+    sub = big[:, ::2]
+    out2 = di.gather(sub, S, tok)
+    assert torch.equal(out2.cpu(), di.gather(sub.contiguous(), S, tok).cpu())
+
+
+# ------------------------------------------------------ small full checks
+
+@pytest.mark.parametrize("flags", [cpr.RUN_FUSED, cpr.RUN_STEPWISE])
+def test_tiny_f32(flags):
+    w = WORKLOADS["tiny_f32"]
+    dev, host = natural_inputs(w)
+    for r in w.ranks:
+        note(f"tiny_f32 rank {r} flags {flags}")
+        o, lse, _ = run_rank(w, dev, r, flags)
+        ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], w.S, w.cp, oracle.ZIGZAG, r, True)
+        compare(o, lse, ro, rl, "f32", f"tiny_f32 r{r}")
+
+
+@pytest.mark.parametrize("flags", [cpr.RUN_FUSED, cpr.RUN_STEPWISE])
+def test_example_4k(flags):
+    w = WORKLOADS["example_4k"]
+    dev, host = natural_inputs(w)
+    for r in (0, 1):
+        note(f"example_4k rank {r} flags {flags}")
+        o, lse, _ = run_rank(w, dev, r, flags)
+        ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], w.S, w.cp, oracle.ZIGZAG, r, True)
+        compare(o, lse, ro, rl, "bf16", f"example_4k r{r}")
+
+
+RAGGED = [
+    # dtype, D, S, cp, layout, causal
+    ("bf16", 128, 1000, 4, "zigzag", True),     # Lq = 250: ragged query and key tiles
+    ("bf16", 64, 77, 3, "zigzag", True),        # padded to 78: a pad query and a pad key
+    ("bf16", 128, 77, 3, "zigzag", False),      # non-causal with a pad token
+    ("bf16", 128, 600, 2, "contiguous", True),  # contiguous causal (imbalanced)
+    ("bf16", 128, 130, 1, "zigzag", True),      # cp = 1: plain causal attention
+    ("bf16", 128, 3000, 8, "zigzag", True),     # many chunks shorter than a tile
+    ("bf16", 64, 513, 2, "contiguous", False),
+    ("f32", 128, 300, 2, "contiguous", False),
+    ("f32", 64, 201, 3, "zigzag", True),
+    ("f32", 128, 10, 4, "zigzag", True),        # every rank mostly padding
+]
+
+
+@pytest.mark.parametrize("case", RAGGED, ids=lambda c: "-".join(map(str, c)))
+def test_ragged_and_padded(case):
+    dtype, D, S, cp, layout, causal = case
+    w = small_workload("ragged", dtype, 1, 2, D, S, cp, layout, causal, seed=zlib.crc32(repr(case).encode()) % 1000)
+    dev, host = natural_inputs(w)
+    lay = lay_code(w)
+    for r in range(cp):
+        for flags in (cpr.RUN_FUSED, cpr.RUN_STEPWISE):
+            o, lse, _ = run_rank(w, dev, r, flags)
+            ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], S, cp, lay, r, causal)
+            compare(o, lse, ro, rl, dtype, f"{case} r{r} f{flags}")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_step_states_match_ring_emulation(dtype, D):
+    """State after each cp_ring_attn_step == the oracle's ring state after the same step."""
+    w = small_workload("steps", dtype, 1, 2, D, 700, 4, "zigzag", True, seed=11)
+    dev, host = natural_inputs(w)
+    r = 2
+    ri = di.prepare_rank(dev["q"], dev["k"], dev["v"], w.S, w.cp, cpr.ZIGZAG, r)
+    lq = ri.lq
+    o_acc = torch.empty(w.B, w.H, lq, D, device="cuda")
+    m = torch.empty(w.B, w.H, lq, device="cuda")
+    l = torch.empty_like(m)
+    cpr.cp_ring_attn_init(o_acc, m, l)
+    tok, pos = oracle.layout(w.S, w.cp, oracle.ZIGZAG)
+    qr = np.zeros((w.B, w.H, len(tok), D))
+    kr, vr = np.zeros_like(qr), np.zeros_like(qr)
+    real = tok < w.S
+    for x, y in ((qr, "q"), (kr, "k"), (vr, "v")):
+        x[:, :, real] = host[y][:, :, tok[real]]
+    sl = slice(r * lq, (r + 1) * lq)
+    _, states = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, w.cp, r, True, keep_states=True)
+    for t in range(w.cp):
+        src = oracle.ring_source(r, t, w.cp)
+        bs = slice(src * lq, (src + 1) * lq)
+        cpr.cp_ring_attn_step(ri.q_local, ri.q_pos, ri.k_ring[:, :, bs], ri.v_ring[:, :, bs], ri.ring_pos[bs], True,
+                              0.0, o_acc, m, l)
+        torch.cuda.synchronize()
+        go, gl = oracle.finalize((o_acc.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()))
+        ro, rl = oracle.finalize(states[t])
+        compare(go, gl, ro, rl, dtype, f"step {t} (block {src})")
+        # the running max itself is the true max of the allowed scores
+        gm, rm = m.cpu().numpy(), states[t][1]
+        assert np.array_equal(np.isneginf(gm), np.isneginf(rm))
+        fin = np.isfinite(rm)
+        assert np.abs(gm[fin] - rm[fin]).max() <= 1e-4
+
+
+# ---------------------------------------------------- state kernels alone
+
+def rand_state(B, H, L, D, seed, empty_frac=0.1):
+    g = np.random.default_rng(seed)
+    o = g.standard_normal((B, H, L, D)).astype(np.float32)
+    m = g.normal(0, 3, (B, H, L)).astype(np.float32)
+    l = g.uniform(0.5, 50, (B, H, L)).astype(np.float32)
+    empty = g.random((B, H, L)) < empty_frac
+    m[empty], l[empty], o[empty] = -np.inf, 0.0, 0.0
+    return o, m, l
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_merge_kernel(D):
+    B, H, L = 2, 3, 333
+    s1, s2 = rand_state(B, H, L, D, 1), rand_state(B, H, L, D, 2)
+    t = [torch.from_numpy(x).cuda() for x in s1]
+    t2 = [torch.from_numpy(x).cuda() for x in s2]
+    cpr.cp_ring_attn_merge(*t, *t2)
+    torch.cuda.synchronize()
+    ro, rm, rl = oracle.merge(s1, s2)
+    go, gm, gl = (x.cpu().numpy() for x in t)
+    assert np.array_equal(np.isneginf(gm), np.isneginf(rm))
+    fin = np.isfinite(rm)
+    assert np.abs(gm[fin] - rm[fin]).max() <= 1e-6
+    assert (np.abs(gl - rl) <= 1e-6 * np.maximum(1, np.abs(rl))).all()
+    assert (np.abs(go - ro) <= 1e-6 * np.maximum(1, np.abs(ro))).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_finalize_and_init_kernels(dtype):
+    B, H, L, D = 1, 4, 130, 128
+    o, m, l = rand_state(B, H, L, D, 3)
+    t = [torch.from_numpy(x).cuda() for x in (o, m, l)]
+    out = torch.empty(B, H, L, D, dtype=TDT[dtype], device="cuda")
+    lse = torch.empty(B, H, L, device="cuda")
+    cpr.cp_ring_attn_finalize(*t, out, lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.finalize((o, m, l))
+    tol = 4e-3 if dtype == "bf16" else 1e-6
+    go = out.float().cpu().numpy()
+    assert (np.abs(go - ro) <= tol * np.maximum(1, np.abs(ro))).all()
+    gl = lse.cpu().numpy()
+    assert np.array_equal(np.isneginf(gl), np.isneginf(rl))
+    assert np.abs(gl[np.isfinite(rl)] - rl[np.isfinite(rl)]).max() <= 1e-5
+    cpr.cp_ring_attn_init(*t)
+    torch.cuda.synchronize()
+    assert (t[0] == 0).all() and torch.isneginf(t[1]).all() and (t[2] == 0).all()
+
+
+# ------------------------------------------------- full-size workloads
+
+def sampled_check(name, flags=cpr.RUN_FUSED, n_rows=None):
+    """Run the workload's rank(s) on the GPU; compare sampled rows with the oracle head by head."""
+    w = WORKLOADS[name]
+    lay = lay_code(w)
+    olay = oracle.ZIGZAG if w.layout == "zigzag" else oracle.CONTIGUOUS
+    s_pad = oracle.padded_len(w.S, w.cp, olay)
+    lq = s_pad // w.cp
+    chunk = lq // 2 if w.layout == "zigzag" else lq
+    rows = sample_rows(lq, chunk, n_rows or 96, seed=w.seed)
+    dev = {t: torch.empty((w.B, w.H, w.S, w.D), dtype=torch.bfloat16, device="cuda") for t in "qkv"}
+    refs = {r: (np.zeros((w.B, w.H, len(rows), w.D)), np.zeros((w.B, w.H, len(rows)))) for r in w.ranks}
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = {t: gen_slice(w, t, b, h) for t in "qkv"}
+            for t in "qkv":
+                dev[t][b, h].copy_(torch.from_numpy(sl[t]).to(torch.bfloat16))
+            for r in w.ranks:
+                ro, rl = oracle.rank_reference(sl["q"][None, None].astype(np.float64),
+                                               sl["k"][None, None].astype(np.float64),
+                                               sl["v"][None, None].astype(np.float64), w.S, w.cp, olay, r, w.causal,
+                                               rows=rows)
+                refs[r][0][b, h], refs[r][1][b, h] = ro[0, 0], rl[0, 0]
+    for r in w.ranks:
+        note(f"{name} rank {r} flags {flags}")
+        o, lse, _ = run_rank(w, dev, r, flags)
+        compare(o[:, :, rows], lse[:, :, rows], refs[r][0], refs[r][1], "bf16", f"{name} r{r} (sampled)")
+    return dev
+
+
+def test_seq32k_cp4_sampled():
+    sampled_check("seq32k_cp4", cpr.RUN_FUSED)
+
+
+def test_seq32k_cp4_stepwise_sampled():
+    sampled_check("seq32k_cp4", cpr.RUN_STEPWISE, n_rows=48)
+
+
+def test_longdoc_noncausal_sampled():
+    sampled_check("longdoc_noncausal", cpr.RUN_FUSED, n_rows=64)
+
+
+def test_million_cp8_sampled():
+    sampled_check("million_cp8", cpr.RUN_FUSED, n_rows=40)
+
+
+def test_million_cp8_zero_keys_closed_form_all_rows():
+    """K = 0 at full size: every allowed score is 0, so LSE = ln(#allowed keys)
+    and O = mean of V over the allowed prefix, for every local row."""
+    w = WORKLOADS["million_cp8"]
+    rank, B, H, D, S = 0, 1, 2, 128, w.S
+    g = torch.Generator().manual_seed(123)
+    v_nat = torch.randn((B, H, S, D), generator=g).to(torch.bfloat16)
+    q_nat = torch.randn((B, H, S, D), generator=g).to(torch.bfloat16)
+    k_nat = torch.zeros((B, H, S, D), dtype=torch.bfloat16)
+    ri = di.prepare_rank(q_nat.cuda(), k_nat.cuda(), v_nat.cuda(), S, w.cp, cpr.ZIGZAG, rank)
+    o = torch.empty_like(ri.q_local)
+    lse = torch.empty(ri.q_local.shape[:3], device="cuda")
+    cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, True, 0.0, o, lse)
+    torch.cuda.synchronize()
+    pos = ri.q_pos.cpu().numpy().astype(np.int64)
+    n_allowed = pos + 1
+    assert np.abs(lse.cpu().numpy() - np.log(n_allowed)[None, None]).max() <= 1e-3
+    csum = np.cumsum(v_nat.float().numpy().astype(np.float64), axis=2)
+    ref = csum[:, :, pos] / n_allowed[None, None, :, None]
+    err = np.abs(o.float().cpu().numpy() - ref).max()
+    note(f"million_cp8 K=0 closed form: max|dO|={err:.3e}")
+    assert err <= 2e-2
+
+
+def test_dropped_block_fails_the_lse_gate():
+    """Folding only cp-1 of the cp blocks must break the LSE bound (the gate has teeth)."""
+    w = WORKLOADS["seq32k_cp4"]
+    r = w.ranks[0]
+    dev, _ = natural_inputs(small_workload("drop", "bf16", 1, 2, 128, 8192, 4, "zigzag", True, seed=7))
+    ri = di.prepare_rank(dev["q"], dev["k"], dev["v"], 8192, 4, cpr.ZIGZAG, r)
+    lq = ri.lq
+    full = torch.empty(1, 2, lq, device="cuda")
+    o = torch.empty_like(ri.q_local)
+    cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, 4, r, True, 0.0, o, full)
+    o_acc = torch.empty(1, 2, lq, 128, device="cuda")
+    m = torch.empty(1, 2, lq, device="cuda")
+    l = torch.empty_like(m)
+    cpr.cp_ring_attn_init(o_acc, m, l)
+    for t in range(3):       # the last block never arrives
+        src = (r - t) % 4
+        bs = slice(src * lq, (src + 1) * lq)
+        cpr.cp_ring_attn_step(ri.q_local, ri.q_pos, ri.k_ring[:, :, bs], ri.v_ring[:, :, bs], ri.ring_pos[bs], True,
+                              0.0, o_acc, m, l)
+    dropped = torch.empty_like(full)
+    cpr.cp_ring_attn_finalize(o_acc, m, l, torch.empty_like(ri.q_local), dropped)
+    torch.cuda.synchronize()
+    assert (dropped - full).abs().max().item() > 1e-3
+
+
+def test_run_is_deterministic():
+    w = small_workload("det", "bf16", 1, 4, 128, 16384, 4, "zigzag", True, seed=9)
+    dev, _ = natural_inputs(w)
+    a, la, _ = run_rank(w, dev, 1, cpr.RUN_FUSED)
+    b, lb, _ = run_rank(w, dev, 1, cpr.RUN_FUSED)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_fused_and_stepwise_agree():
+    w = small_workload("agree", "bf16", 1, 2, 128, 8192, 4, "zigzag", True, seed=10)
+    dev, _ = natural_inputs(w)
+    a, la, _ = run_rank(w, dev, 3, cpr.RUN_FUSED)
+    b, lb, _ = run_rank(w, dev, 3, cpr.RUN_STEPWISE)
+    assert np.abs(a - b).max() <= 1e-2 and np.abs(la - lb).max() <= 1e-4
