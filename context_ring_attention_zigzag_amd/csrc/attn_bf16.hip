@@ -12,15 +12,34 @@
 // Mapping to the hardware:
 //  * a workgroup owns BM = 32*NW queries of one (b, h); each wavefront owns 32
 //    of them and keeps their Q rows in VGPRs for the whole pass;
-//  * keys stream through LDS in tiles of BN = 64, double-buffered, loaded with
-//    coalesced 16-byte global loads and XOR-swizzled against bank conflicts;
+//  * two wave groups (waves [0, NW/2) and [NW/2, NW), one wave of each per
+//    SIMD) run the same key-tile sequence one phase apart. Each tile takes two
+//    phases: an MFMA phase (P*V of the previous tile, then S^T = K Q^T of this
+//    one) and a VALU phase (mask, row max, exponentials, row sums). While one
+//    group is in its MFMA phase the other is in its VALU phase, so the matrix
+//    cores and the vector ALUs of every SIMD work at the same time; a
+//    workgroup barrier separates consecutive phases;
+//  * keys stream through LDS in tiles of BN = 64 with direct global->LDS
+//    16-byte loads (global_load_lds_dwordx4), issued two phases before their
+//    first use into double-buffered K and V tiles;
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: lane l then holds query l%32 and 16 of the 32
 //    keys of a 32x32 block, so the per-query max and sum are lane-local plus
 //    one exchange between the two half-waves (v_permlane32_swap);
 //  * O^T = V^T P^T on the same MFMA: the probabilities leave the score
-//    accumulators already in the B-operand layout (rounded to bf16), and V^T
-//    comes straight from the row-major V tile through ds_read_b64_tr_b16;
+//    accumulators already in the B-operand layout (v_cvt_pk_bf16_f32, round
+//    to nearest even), and V^T comes from the V tile through ds_read_b64_tr_b16;
+//    the row sums add the float32 probabilities before rounding (a sum of the
+//    rounded values would carry their 2^-9 relative error into the LSE of rows
+//    that see few keys);
+//  * lazy rescaling: exponents are taken against a reference max that is only
+//    raised when a row's max exceeds it by more than kTau (log2 units), so the
+//    O/l rescale is almost never executed; the result is unchanged because O
+//    and l always share the same reference;
+//  * every LDS read of the MFMA phase is one per-lane base register plus a
+//    compile-time offset: K is row-major with a 16-byte-chunk XOR swizzle,
+//    V is stored as 4-key x 32-column sub-blocks that a 32-lane transposed read
+//    covers without bank conflicts;
 //  * (query tile, key tile) pairs are classified from their position ranges
 //    into skip / full / mixed; skipped tiles are neither loaded nor computed,
 //    full tiles need no element mask;
@@ -28,29 +47,50 @@
 //    same XCD (shared L2), heaviest query tiles first.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace cpring {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
 typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef short s16x8 __attribute__((__vector_size__(8 * sizeof(short))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kTau = 8.0f;    // lazy-rescale threshold: probabilities stay below 2^kTau
 constexpr int kXcds = 8;        // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 constexpr int kBN = 64;         // keys per tile
-constexpr int kMaxTiles = 4096; // tiles classified per pass (bitmask of kMaxTiles/64 words)
+constexpr int kMaxTiles = 4096; // key tiles classified per segment of a KV block
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  // round to nearest even (finite inputs)
-  uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
-  a += 0x7fffu + ((a >> 16) & 1u);
-  b += 0x7fffu + ((b >> 16) & 1u);
-  return (a >> 16) | (b & 0xffff0000u);
+template <int D, int NW>
+struct Cfg {
+  static constexpr int kThreads = NW * 64;
+  static constexpr int kBM = 32 * NW;              // queries per workgroup
+  static constexpr int kKSteps = D / 16;           // MFMA steps over the head dim
+  static constexpr int kDTiles = D / 32;           // 32-row tiles of O^T
+  static constexpr int kChunks = D / 8;            // 16-byte chunks per K/V row
+  static constexpr int kDq = D / 32;               // 32-column V sub-blocks per 4-key group
+  static constexpr int kTileChunks = kBN * kChunks;
+  static constexpr int kLoadsPerWave = kTileChunks / (64 * NW);   // wave-wide 16-byte loads per tensor
+  static constexpr int kNB = 4 * kDTiles;          // MFMAs of O^T per tile
+  static_assert(NW % 2 == 0, "two wave groups");
+  static_assert(kLoadsPerWave >= 1 && kTileChunks % (64 * NW) == 0, "tile/threads mismatch");
+};
+
+// K tile: row-major, physical 16-byte chunk = logical chunk XOR a function of
+// the row, so the 16 consecutive rows one A-operand read touches per 16 lanes
+// hit 16 different bank groups. (An involution: also maps physical to logical.)
+template <int D>
+__device__ __forceinline__ int swz_k(int row, int chunk) {
+  if constexpr (D == 128) return chunk ^ (row & 15);
+  else return chunk ^ ((row >> 1) & 7);
 }
 
 __device__ __forceinline__ float other_half_max(float x) {
@@ -75,38 +115,42 @@ __device__ __forceinline__ int wave_max(int x) {
   return x;
 }
 
-template <int D, int NW>
-struct Cfg {
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kBM = 32 * NW;          // queries per workgroup
-  static constexpr int kKSteps = D / 16;       // MFMA steps over the head dim
-  static constexpr int kDTiles = D / 32;       // 32-row tiles of O^T
-  static constexpr int kChunksPerRow = D / 8;  // 16-byte chunks per K/V row
-  static constexpr int kLoads = kBN * kChunksPerRow / kThreads;  // 16-byte loads per thread per tensor
-  static_assert(kLoads >= 1 && kBN * kChunksPerRow % kThreads == 0, "tile/threads mismatch");
-};
+// Workgroup barrier without a memory fence: this wave's LDS accesses are
+// complete, its in-flight global->LDS loads are not waited for (each wave
+// waits for its own one phase later, before the barrier that precedes their
+// first use). The memory clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// LDS swizzles (16-byte chunk index XOR a function of the row).
-// K: lanes 0..7 of an A-operand read hit rows r..r+7 at one chunk -> XOR row%8.
-// V: a 16-lane transpose read covers 4 consecutive rows x 2 chunks -> XOR 2*(row%4).
-__device__ __forceinline__ int swz_k(int row, int chunk) { return chunk ^ (row & 7); }
-__device__ __forceinline__ int swz_v(int row, int chunk) { return chunk ^ ((row & 3) << 1); }
+template <int N>
+using ic = std::integral_constant<int, N>;
+
+__device__ __forceinline__ int mod3_next(int x) { return x == 2 ? 0 : x + 1; }
 
 template <int D, int NW>
-__global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   using C = Cfg<D, NW>;
   constexpr int kThreads = C::kThreads;
+  constexpr int kDq = C::kDq;
 
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kBN * D];
-  __shared__ __attribute__((aligned(16))) int32_t pos_lds[2][kBN];
+  // Separate arrays per K/V buffer so that every MFMA-phase access names its
+  // buffer statically; three position buffers (positions are read one phase
+  // longer than K).
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds0[kBN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds1[kBN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds0[kBN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds1[kBN * D];
+  __shared__ __attribute__((aligned(16))) int32_t pos_lds[3][kBN];
   __shared__ uint64_t keep_w[kMaxTiles / 64];
   __shared__ uint64_t mixed_w[kMaxTiles / 64];
+  __shared__ uint8_t flags8[kMaxTiles];
   __shared__ int32_t qrange[2][NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  const int group = wave / (NW / 2);   // 0 leads, 1 trails by one phase
   const int ql = lane & 31;   // query column owned by this lane
   const int hh = lane >> 5;   // half-wave
 
@@ -164,9 +208,10 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   }
 
   // ---- running state: O^T[d = 32*dt + 8*i + 4*hh + j][query] in ot[dt][4*i + j]
+  // m_ref: reference max (log2 units of the scaled score) the exponents are taken
+  // against; m_true: the true running max; lsum0/1: this half-wave's share of l.
   f32x16 ot[C::kDTiles];
-  float m2 = -INFINITY;   // running max, log2 units of the scaled score
-  float lsum = 0.f;       // this half-wave's share of the running sum
+  float m_ref = -INFINITY, m_true = -INFINITY, lsum0 = 0.f, lsum1 = 0.f;
   const int64_t srow = (int64_t)bh * a.Lq + q_idx;
   if (a.load_state && q_in) {
 #pragma unroll
@@ -180,14 +225,16 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
         ot[dt][4 * i + 3] = x.w;
       }
     const float mn = a.m[srow];
-    m2 = (mn == -INFINITY) ? -INFINITY : mn * kLog2e;
-    lsum = hh == 0 ? a.l[srow] : 0.f;
+    m_ref = (mn == -INFINITY) ? -INFINITY : mn * kLog2e;
+    m_true = m_ref;
+    lsum0 = hh == 0 ? a.l[srow] : 0.f;
   } else {
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) ot[dt][i] = 0.f;
   }
+  float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;   // finite stand-in while nothing is allowed yet
 
   const float c2 = a.scale * kLog2e;   // score -> log2 units
   const bool wg_has_queries = qmax >= 0;
@@ -195,6 +242,17 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
   const __bf16* kbh = static_cast<const __bf16*>(a.k) + b * a.k_sb + h * a.k_sh;
   const __bf16* vbh = static_cast<const __bf16*>(a.v) + b * a.v_sb + h * a.v_sh;
   const int n_kt = (a.Lk + kBN - 1) / kBN;
+
+  // LDS read offsets (elements), loop invariant.
+  // K, A operand of S^T: lane (ql, hh) reads row 32*kt + ql, logical chunk 2*kk + hh.
+  int koff[C::kKSteps];
+#pragma unroll
+  for (int kk = 0; kk < C::kKSteps; ++kk) koff[kk] = ql * D + swz_k<D>(ql, 2 * kk + hh) * 8;
+  // V, A operand of O^T via the transposed read: lane (g, gi) of 16-lane group g
+  // reads 4 columns of key 16*ch + 4*(g>>1) + (gi>>2) (+8 for the second read),
+  // columns 32*dt + 16*(g&1) + 4*(gi&3). Element (key, d) of the tile sits at
+  // ((key/4)*kDq + d/32)*128 + (key%4)*32 + d%32.
+  const int vbase = (lane >> 5) * kDq * 128 + ((lane & 15) >> 2) * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
   for (int t = 0; t < a.nblocks && wg_has_queries; ++t) {
     int src = (a.rank - t) % a.cp;
@@ -207,36 +265,54 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     for (int seg0 = 0; seg0 < n_kt; seg0 += kMaxTiles) {
       const int nseg = min(kMaxTiles, n_kt - seg0);
 
-      // ---- classify the segment's key tiles against this query tile
-      __syncthreads();
-      for (int tt = tid; tt < ((nseg + 63) & ~63); tt += kThreads) {
-        bool keep = false, mixed = false;
+      // ---- classify the segment's key tiles: 16 lanes per tile, 4 positions each
+      bar();   // the previous segment is done with flags8 / keep_w / the buffers
+      for (int base = 0; base < nseg; base += kThreads / 16) {
+        const int tt = base + (tid >> 4);
+        const int g16 = tid & 15;
+        int kmin = INT_MAX, kmax = -1, pad = 0;
         if (tt < nseg) {
-          const int k0 = (seg0 + tt) * kBN;
-          const int k1 = min(k0 + kBN, a.Lk);
-          int kmin = INT_MAX, kmax = -1;
-          bool pad = (k1 - k0) < kBN;
-          for (int j = k0; j < k1; ++j) {
-            const int p = posb[j];
-            pad |= p < 0;
-            kmin = (p >= 0 && p < kmin) ? p : kmin;
-            kmax = p > kmax ? p : kmax;
+          const int k0 = (seg0 + tt) * kBN + 4 * g16;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = k0 + e;
+            if (j < a.Lk) {
+              const int p = posb[j];
+              pad |= p < 0;
+              kmin = (p >= 0 && p < kmin) ? p : kmin;
+              kmax = p > kmax ? p : kmax;
+            } else {
+              pad = 1;
+            }
           }
-          keep = kmax >= 0 && (!a.causal || kmin <= qmax);
-          const bool full = !pad && (!a.causal || kmax <= qmin);
-          mixed = keep && !full;
         }
-        const uint64_t kw = __ballot(keep);
-        const uint64_t mw = __ballot(mixed);
+#pragma unroll
+        for (int o = 8; o >= 1; o >>= 1) {
+          kmin = min(kmin, __shfl_xor(kmin, o));
+          kmax = max(kmax, __shfl_xor(kmax, o));
+          pad |= __shfl_xor(pad, o);
+        }
+        if (g16 == 0 && tt < nseg) {
+          const bool keep = kmax >= 0 && (!a.causal || kmin <= qmax);
+          const bool full = !pad && (!a.causal || kmax <= qmin);
+          flags8[tt] = (uint8_t)((keep ? 1 : 0) | ((keep && !full) ? 2 : 0));
+        }
+      }
+      bar();
+      for (int tt = tid; tt < ((nseg + 63) & ~63); tt += kThreads) {
+        const int f = tt < nseg ? flags8[tt] : 0;
+        const uint64_t kw = __ballot(f & 1);
+        const uint64_t mw = __ballot(f & 2);
         if (lane == 0) {
           keep_w[tt >> 6] = kw;
           mixed_w[tt >> 6] = mw;
         }
       }
-      __syncthreads();
+      bar();
 
       const int nwords = (nseg + 63) >> 6;
-      auto next_kept = [&](int j) -> int {   // first kept tile index > j, or nseg
+      auto next_kept = [&](int j) __attribute__((always_inline)) -> int {   // first kept tile index > j, or nseg
+        if (j >= nseg) return nseg;
         int w = (j + 1) >> 6;
         if (w >= nwords) return nseg;
         uint64_t bits = keep_w[w] & (~0ull << ((j + 1) & 63));
@@ -244,151 +320,243 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
           if (++w >= nwords) return nseg;
           bits = keep_w[w];
         }
-        return min(nseg, (w << 6) + (int)__builtin_ctzll(bits));
+        return __builtin_amdgcn_readfirstlane(min(nseg, (w << 6) + (int)__builtin_ctzll(bits)));
       };
+      auto is_mixed = [&](int j) __attribute__((always_inline)) -> bool { return (mixed_w[j >> 6] >> (j & 63)) & 1ull; };
 
-      uint4 kreg[C::kLoads], vreg[C::kLoads];
-      int32_t preg = -1;
-      auto load_tile = [&](int j) {
+      // ---- direct global -> LDS loads (this wave's share of a tile): lane
+      // `lane` of wave-load `blk` fills the 16-byte LDS chunk blk*64 + lane with
+      // the global chunk the layout puts there. Rows past Lk re-read row Lk-1
+      // (finite data; those keys are masked, so their P is exactly 0). A tile
+      // index >= nseg (past the last kept tile) loads nothing.
+      auto issue_k = [&](int j, auto slot, int pslot) __attribute__((always_inline)) {
+        if (j >= nseg) return;
         const int r_base = (seg0 + j) * kBN;
+        __bf16* dst = decltype(slot)::value ? k_lds1 : k_lds0;
 #pragma unroll
-        for (int u = 0; u < C::kLoads; ++u) {
-          const int cidx = tid + u * kThreads;
-          const int row = cidx / C::kChunksPerRow;
-          const int ch = cidx % C::kChunksPerRow;
-          if (r_base + row < a.Lk) {
-            kreg[u] = *reinterpret_cast<const uint4*>(kb + (int64_t)(r_base + row) * a.k_sl + ch * 8);
-            vreg[u] = *reinterpret_cast<const uint4*>(vb + (int64_t)(r_base + row) * a.v_sl + ch * 8);
-          } else {
-            kreg[u] = make_uint4(0u, 0u, 0u, 0u);
-            vreg[u] = make_uint4(0u, 0u, 0u, 0u);
-          }
+        for (int u = 0; u < C::kLoadsPerWave; ++u) {
+          const int blk = wave * C::kLoadsPerWave + u;
+          const int s = blk * 64 + lane;
+          const int row = s / C::kChunks;
+          const int lch = swz_k<D>(row, s % C::kChunks);
+          const int grow = min(r_base + row, a.Lk - 1);
+          __builtin_amdgcn_global_load_lds(kb + (int64_t)grow * a.k_sl + lch * 8, (lds_void*)(dst + blk * 512), 16,
+                                           0, 0);
         }
-        if (tid < kBN) preg = (r_base + tid < a.Lk) ? posb[r_base + tid] : -1;
+        if (wave == NW - 1) {
+          const int r = min(r_base + lane, a.Lk - 1);
+          __builtin_amdgcn_global_load_lds(posb + r, (lds_void*)&pos_lds[pslot][0], 4, 0, 0);
+        }
       };
-      auto store_tile = [&](int buf) {
+      auto issue_v = [&](int j, auto slot) __attribute__((always_inline)) {
+        if (j >= nseg) return;
+        const int r_base = (seg0 + j) * kBN;
+        __bf16* dst = decltype(slot)::value ? v_lds1 : v_lds0;
 #pragma unroll
-        for (int u = 0; u < C::kLoads; ++u) {
-          const int cidx = tid + u * kThreads;
-          const int row = cidx / C::kChunksPerRow;
-          const int ch = cidx % C::kChunksPerRow;
-          *reinterpret_cast<uint4*>(&k_lds[buf][row * D + swz_k(row, ch) * 8]) = kreg[u];
-          *reinterpret_cast<uint4*>(&v_lds[buf][row * D + swz_v(row, ch) * 8]) = vreg[u];
+        for (int u = 0; u < C::kLoadsPerWave; ++u) {
+          const int blk = wave * C::kLoadsPerWave + u;
+          const int s = blk * 64 + lane;
+          const int sb = s >> 4, q = s & 15;
+          const int row = 4 * (sb / kDq) + (q >> 2);
+          const int lch = 4 * (sb % kDq) + (q & 3);
+          const int grow = min(r_base + row, a.Lk - 1);
+          __builtin_amdgcn_global_load_lds(vb + (int64_t)grow * a.v_sl + lch * 8, (lds_void*)(dst + blk * 512), 16,
+                                           0, 0);
         }
-        if (tid < kBN) pos_lds[buf][tid] = preg;
       };
 
-      int j = next_kept(-1);
-      if (j < nseg) {
-        load_tile(j);
-        store_tile(0);
-      }
-      __syncthreads();
-      int buf = 0;
-      while (j < nseg) {
-        const int jn = next_kept(j);
-        const bool has_next = jn < nseg;
-        const bool mixed = (mixed_w[j >> 6] >> (j & 63)) & 1ull;
-        if (has_next) load_tile(jn);
-
-        // ---- S^T = K Q^T for two 32-key sub-tiles
-        const __bf16* kl = k_lds[buf];
-        f32x16 s[2];
+      // ---- MFMA phase pieces
+      // S^T = K Q^T for two 32-key sub-tiles; K fragments fetched two steps ahead
+      auto qk = [&](auto slot, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        const __bf16* kl = decltype(slot)::value ? k_lds1 : k_lds0;
+        bf16x8 kf[3][2];
+        auto fetch = [&](int kk) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+          for (int kt = 0; kt < 2; ++kt)
+            kf[kk % 3][kt] = *reinterpret_cast<const bf16x8*>(kl + kt * 32 * D + koff[kk]);
+        };
+        fetch(0);
+        fetch(1);
 #pragma unroll
         for (int kk = 0; kk < C::kKSteps; ++kk) {
+          if (kk + 2 < C::kKSteps) fetch(kk + 2);
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
-            const int row = kt * 32 + ql;
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + row * D + swz_k(row, 2 * kk + hh) * 8);
-            s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[kk], s[kt], 0, 0, 0);
+            if (kk == 0) {
+              const f32x16 z = {};
+              s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][kt], qf[0], z, 0, 0, 0);
+            } else {
+              s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % 3][kt], qf[kk], s[kt], 0, 0, 0);
+            }
           }
         }
+      };
+      // O^T += V^T P^T; V fragments (two transposed reads each) fetched two MFMAs ahead
+      auto pv = [&](auto slot, const bf16x8 (&pb)[4]) __attribute__((always_inline)) {
+        const __bf16* vl = decltype(slot)::value ? v_lds1 : v_lds0;
+        s16x4 vf[3][2];
+        auto fetch = [&](int m) __attribute__((always_inline)) {
+          const int ch = m / C::kDTiles, dt = m % C::kDTiles;
+          const __bf16* p = vl + vbase + (4 * ch * kDq + dt) * 128;
+          vf[m % 3][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          vf[m % 3][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2 * kDq * 128));
+        };
+        fetch(0);
+        fetch(1);
+#pragma unroll
+        for (int m = 0; m < C::kNB; ++m) {
+          if (m + 2 < C::kNB) fetch(m + 2);
+          const int ch = m / C::kDTiles, dt = m % C::kDTiles;
+          const s16x8 vv = __builtin_shufflevector(vf[m % 3][0], vf[m % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          ot[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[ch], ot[dt], 0, 0, 0);
+        }
+      };
 
-        // ---- mask (only tiles straddling the causal boundary or holding pads)
-        if (mixed) {
+      // ---- VALU phase: mask, max, rescale, exponentials, row sums
+      auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pb)[4], int j, int pslot) __attribute__((always_inline)) {
+        if (is_mixed(j)) {
+          // element mask of a tile straddling the causal boundary or holding
+          // pads / rows past Lk
+          const int32_t* pl = &pos_lds[pslot][0];
+          const int rem = a.Lk - (seg0 + j) * kBN;   // keys of this tile that exist
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int4 p = *reinterpret_cast<const int4*>(&pos_lds[buf][kt * 32 + 8 * i + 4 * hh]);
+              const int key0 = kt * 32 + 8 * i + 4 * hh;
+              const int4 p = *reinterpret_cast<const int4*>(pl + key0);
               const int pk[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
               for (int jj = 0; jj < 4; ++jj) {
-                const bool ok = pk[jj] >= 0 && qp >= 0 && (!a.causal || pk[jj] <= qp);
+                const bool ok = key0 + jj < rem && pk[jj] >= 0 && qp >= 0 && (!a.causal || pk[jj] <= qp);
                 s[kt][4 * i + jj] = ok ? s[kt][4 * i + jj] : -INFINITY;
               }
             }
         }
-
-        // ---- online softmax (log2 units)
         float mx = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
         mx = other_half_max(mx);
-        const float m_new = fmaxf(m2, mx * c2);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        if (__any(m_new > m2)) {
-          const float alpha = __builtin_amdgcn_exp2f(m2 - m_use);
+        // raise the reference max where this tile's max outgrew it by more than kTau
+        const float mt = mx * c2;
+        m_true = fmaxf(m_true, mt);
+        const bool need = mt > m_ref + kTau;
+        if (__any(need)) {
+          const float m_new = need ? mt : m_ref;
+          const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
 #pragma unroll
           for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) ot[dt][i] *= alpha;
-          lsum *= alpha;
+          lsum0 *= alpha;
+          lsum1 *= alpha;
+          m_ref = m_new;
+          m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
         }
-        m2 = m_new;
-
-        // probabilities -> bf16 B operand of O^T += V^T P^T (16 keys per chunk)
-        bf16x8 pb[4];
+        // P = 2^(s*c2 - m_ref) rounded to bf16, in the B-operand layout of
+        // O^T += V^T P^T (16 keys per chunk); l accumulates the same values
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
+        for (int c = 0; c < 4; ++c) {
+          uint32_t w4[4];
 #pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            float e[8];
-#pragma unroll
-            for (int x = 0; x < 8; ++x) {
-              e[x] = __builtin_amdgcn_exp2f(fmaf(s[kt][8 * p + x], c2, -m_use));
-              lsum += e[x];
-            }
-            uint32_t w4[4] = {pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]), pack_bf16x2(e[4], e[5]),
-                              pack_bf16x2(e[6], e[7])};
-            pb[2 * kt + p] = __builtin_bit_cast(bf16x8, w4);
+          for (int x = 0; x < 4; ++x) {
+            const float e0 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + 2 * x], c2, -m_use));
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + 2 * x + 1], c2, -m_use));
+            const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+            lsum0 += e0;
+            lsum1 += e1;
+            w4[x] = __builtin_bit_cast(uint32_t, pr);
           }
-
-        // ---- O^T += V^T P^T; V^T rows via the LDS transpose read
-        const __bf16* vl = v_lds[buf];
-        const int g = lane >> 4, gi = lane & 15;
-#pragma unroll
-        for (int ch = 0; ch < 4; ++ch) {
-#pragma unroll
-          for (int dt = 0; dt < C::kDTiles; ++dt) {
-            const int row_a = 16 * ch + 4 * (g >> 1) + (gi >> 2);
-            const int row_b = row_a + 8;
-            const int col = 32 * dt + 16 * (g & 1) + 4 * (gi & 3);
-            const __bf16* pa = vl + row_a * D + swz_v(row_a, col >> 3) * 8 + (col & 7);
-            const __bf16* pbp = vl + row_b * D + swz_v(row_b, col >> 3) * 8 + (col & 7);
-            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pa);
-            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)pbp);
-            const s16x8 vv = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            ot[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[ch], ot[dt], 0, 0, 0);
-          }
+          pb[c] = __builtin_bit_cast(bf16x8, w4);
         }
+      };
 
-        if (has_next) store_tile(buf ^ 1);
-        __syncthreads();
-        buf ^= 1;
-        j = jn;
+      // Kept tiles j_0, j_1, ... in order; tile u uses K buffer u&1, V buffer
+      // u&1 and position buffer u%3. Global phases: group 0 runs the MFMA phase
+      // of tile u in phase 2u and its VALU phase in 2u+1; group 1 runs them in
+      // 2u+1 and 2u+2. In phase 2u both groups load K and positions of tile u+1
+      // and V of tile u (group 0 at the start of its MFMA phase of tile u,
+      // group 1 at the start of its VALU phase of tile u-1); each wave waits for
+      // its loads before the barrier that ends phase 2u+1.
+      int ju = next_kept(-1);
+      if (ju >= nseg) continue;   // uniform: every wave sees the same bitmask
+      int ju1 = next_kept(ju);
+      int ju2 = next_kept(ju1);
+
+      f32x16 s[2];
+      bf16x8 pb[4];
+
+      // prologue: K of tile 0, then tile 0 (no P*V yet)
+      issue_k(ju, ic<0>{}, 0);
+      wait_vmem();
+      bar();
+      if (group == 0) {
+        issue_k(ju1, ic<1>{}, 1);
+        issue_v(ju, ic<0>{});
+        qk(ic<0>{}, s);
+        bar();
+        softmax(s, pb, ju, 0);
+        wait_vmem();
+        bar();
+      } else {
+        issue_k(ju1, ic<1>{}, 1);
+        issue_v(ju, ic<0>{});
+        bar();
+        qk(ic<0>{}, s);
+        wait_vmem();
+        bar();
+        issue_k(ju2, ic<0>{}, 2);
+        issue_v(ju1, ic<1>{});
+        softmax(s, pb, ju, 0);
+        bar();
       }
+      ju = ju1;
+      ju1 = ju2;
+      ju2 = next_kept(ju2);
+
+      // tile u >= 1; after the last kept tile one more MFMA phase finishes P*V
+      int pu = 1;   // u % 3
+      auto tile = [&](auto kslot) __attribute__((always_inline)) -> bool {
+        constexpr int KS = decltype(kslot)::value;   // u & 1
+        const bool has = ju < nseg;
+        const int pu1 = mod3_next(pu), pu2 = mod3_next(pu1);
+        if (group == 0) {
+          issue_k(ju1, ic<KS ^ 1>{}, pu1);
+          issue_v(ju, ic<KS>{});
+          pv(ic<KS ^ 1>{}, pb);
+          qk(ic<KS>{}, s);   // stale K when !has: computed, never used
+          bar();
+          if (has) softmax(s, pb, ju, pu);
+          wait_vmem();
+          bar();
+        } else {
+          pv(ic<KS ^ 1>{}, pb);
+          qk(ic<KS>{}, s);
+          wait_vmem();
+          bar();
+          issue_k(ju2, ic<KS>{}, pu2);
+          issue_v(ju1, ic<KS ^ 1>{});
+          if (has) softmax(s, pb, ju, pu);
+          bar();
+        }
+        pu = pu1;
+        ju = ju1;
+        ju1 = ju2;
+        ju2 = next_kept(ju2);
+        return has;
+      };
+      while (true) {
+        if (!tile(ic<1>{})) break;
+        if (!tile(ic<0>{})) break;
+      }
+      if (group == 0) bar();   // group 1 ran one extra barrier at the start
     }
   }
 
   // ---- epilogue
-  const float l_tot = other_half_sum(lsum);
+  const float l_tot = other_half_sum(lsum0 + lsum1);
   if (!q_in) return;
   const bool has = qp >= 0 && l_tot > 0.f;
   if (a.finalize) {
@@ -398,24 +566,28 @@ __global__ void __launch_bounds__(NW * 64, 2) attn_bf16_kernel(AttnArgs a) {
     for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        const bf16x2 w0 = {(__bf16)(ot[dt][4 * i + 0] * inv), (__bf16)(ot[dt][4 * i + 1] * inv)};
+        const bf16x2 w1 = {(__bf16)(ot[dt][4 * i + 2] * inv), (__bf16)(ot[dt][4 * i + 3] * inv)};
         uint2 w;
-        w.x = pack_bf16x2(ot[dt][4 * i + 0] * inv, ot[dt][4 * i + 1] * inv);
-        w.y = pack_bf16x2(ot[dt][4 * i + 2] * inv, ot[dt][4 * i + 3] * inv);
+        w.x = __builtin_bit_cast(uint32_t, w0);
+        w.y = __builtin_bit_cast(uint32_t, w1);
         *reinterpret_cast<uint2*>(out + 32 * dt + 8 * i + 4 * hh) = w;
       }
-    if (a.lse && hh == 0) a.lse[srow] = has ? m2 * kLn2 + logf(l_tot) : -INFINITY;
+    if (a.lse && hh == 0) a.lse[srow] = has ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   } else {
+    // hand back the state against the true running max: O and l scale by 2^(m_ref - m_true) <= 1
+    const float beta = has ? __builtin_amdgcn_exp2f(m_ref - m_true) : 0.f;
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float4 x = make_float4(ot[dt][4 * i + 0], ot[dt][4 * i + 1], ot[dt][4 * i + 2], ot[dt][4 * i + 3]);
-        if (qp < 0) x = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 x = make_float4(ot[dt][4 * i + 0] * beta, ot[dt][4 * i + 1] * beta, ot[dt][4 * i + 2] * beta,
+                                     ot[dt][4 * i + 3] * beta);
         *reinterpret_cast<float4*>(a.o_acc + srow * D + 32 * dt + 8 * i + 4 * hh) = x;
       }
     if (hh == 0) {
-      a.m[srow] = (qp >= 0 && m2 != -INFINITY) ? m2 * kLn2 : -INFINITY;
-      a.l[srow] = qp >= 0 ? l_tot : 0.f;
+      a.m[srow] = has ? m_true * kLn2 : -INFINITY;
+      a.l[srow] = has ? l_tot * beta : 0.f;
     }
   }
 }
@@ -431,10 +603,8 @@ hipError_t launch(const AttnArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
-  if (a.D == 64) return launch<64, 4>(a, st);
-  const long tiles8 = (long)a.B * a.H * ((a.Lq + 255) / 256);
-  if (tiles8 >= 512) return launch<128, 8>(a, st);
-  return launch<128, 4>(a, st);
+  if (a.D == 64) return launch<64, 8>(a, st);
+  return launch<128, 8>(a, st);
 }
 
 }  // namespace cpring
