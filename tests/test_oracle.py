@@ -368,3 +368,50 @@ def test_planted_wrong_chunk_pairing_is_caught(monkeypatch, golden_dir):
     monkeypatch.setattr(oracle, "layout", bad_layout)
     with pytest.raises(AssertionError):
         test_layout_matches_pages_cp4_table(golden_dir)
+
+
+def test_planted_wrong_rescale_sign_is_caught(monkeypatch):
+    """A fold that rescales earlier partial sums by exp(m_new - m) instead of
+    exp(m - m_new) must break the ring == full-attention pin."""
+    def bad_fold(state, q, k_blk, v_blk, q_pos, k_pos, causal, scale=None):
+        o, m, l = (np.array(x, dtype=np.float64) for x in state)
+        scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+        ok = ora.allowed_mask(q_pos, k_pos, causal)
+        for b in range(q.shape[0]):
+            for h in range(q.shape[1]):
+                s = np.where(ok, scale * (q[b, h] @ k_blk[b, h].T), -np.inf)
+                m_new = np.maximum(m[b, h], s.max(axis=1))
+                m_use = np.where(np.isfinite(m_new), m_new, 0.0)
+                alpha = np.where(np.isfinite(m[b, h]), np.exp(m_use - m[b, h]), 0.0)   # planted: sign flipped
+                p = np.where(ok, np.exp(s - m_use[:, None]), 0.0)
+                l[b, h] = alpha * l[b, h] + p.sum(axis=1)
+                o[b, h] = alpha[:, None] * o[b, h] + p @ v_blk[b, h]
+                m[b, h] = m_new
+        return o, m, l
+    w = small_workload("t", "f32", 1, 1, 8, 64, 4, "zigzag", True, seed=6)
+    q, k, v, qr, kr, vr, tok, pos, lay = ring_inputs(w)
+    lr = len(tok) // w.cp
+    r = 3
+    sl = slice(r * lr, (r + 1) * lr)
+    ro, rl = oracle.rank_reference(q, k, v, w.S, w.cp, lay, r, True)
+    good, _ = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, w.cp, r, True)
+    assert np.abs(good - ro).max() < 1e-12
+    monkeypatch.setattr(ora, "fold_block", bad_fold)
+    bad, _ = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, w.cp, r, True)
+    assert np.abs(bad - ro).max() > 1e-3
+
+
+def test_planted_swapped_operands_are_caught(monkeypatch):
+    """Attention that multiplies P by K instead of V must fail the torch SDPA pin."""
+    orig = ora._attend_rows
+
+    def swapped(q, k, v, q_pos, k_pos, causal, scale):
+        return orig(q, k, k, q_pos, k_pos, causal, scale)
+    monkeypatch.setattr(ora, "_attend_rows", swapped)
+    s, d = 16, 8
+    q, k, v = rnd((1, 2, s, d), 50), rnd((1, 2, s, d), 51), rnd((1, 2, s, d), 52)
+    pos = np.arange(s)
+    o, _ = oracle.full_attention(q, k, v, pos, pos, True)
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
+                                                           torch.from_numpy(v), is_causal=True).numpy()
+    assert np.abs(o - ref).max() > 1e-3
