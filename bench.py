@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0    # MI355X published dense bf16 MFMA peak
 PEAK_F32_TFLOPS = 157.3      # MI355X published fp32 vector peak
+PEAK_HBM_GBS = 8000.0        # MI355X published HBM3E bandwidth
 KERNEL_SRC = os.path.join(ROOT, "context_ring_attention_zigzag_amd", "csrc", "attn_bf16.hip")
 KERNEL_NAME = "attn_bf16_kernel"
 
@@ -63,7 +64,11 @@ def traffic_from_profile(workload: str):
 
 
 def cpu_baseline(w, rank: int, budget_s: float):
-    """Time the fp64 oracle on sampled local rows of one (b, h) slice for about ``budget_s`` seconds."""
+    """Time the fp64 oracle on local rows of the workload for about ``budget_s`` seconds.
+
+    Walks (b, h) slices in order and, inside each, the rank's local rows in a seeded order, 64 rows per oracle
+    call, until the budget is spent. The rate is allowed-pair flops (4*D per pair) per second of oracle time.
+    """
     import numpy as np
     import oracle
     from seeded_inputs import gen_slice
@@ -73,27 +78,68 @@ def cpu_baseline(w, rank: int, budget_s: float):
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
     lay = oracle.ZIGZAG if w.layout == "zigzag" else oracle.CONTIGUOUS
-    q = gen_slice(w, "q", 0, 0)[None, None].astype(np.float64)
-    k = gen_slice(w, "k", 0, 0)[None, None].astype(np.float64)
-    v = gen_slice(w, "v", 0, 0)[None, None].astype(np.float64)
     tok, pos = oracle.layout(w.S, w.cp, lay)
     lq = len(tok) // w.cp
     local_pos = pos[rank * lq:(rank + 1) * lq]
-    rng = np.random.default_rng(0)
-    order = rng.permutation(lq)
-    done, flops, t_used = 0, 0.0, 0.0
+    order = np.random.default_rng(0).permutation(lq)
+    rows_done, slices, flops, t_used = 0, 0, 0.0, 0.0
     chunk = 64
-    while t_used < budget_s and done < lq:
-        rows = np.sort(order[done:done + chunk])
-        t0 = time.perf_counter()
-        oracle.rank_reference(q, k, v, w.S, w.cp, lay, rank, w.causal, rows=rows)
-        t_used += time.perf_counter() - t0
-        p = local_pos[rows]
-        n_keys = np.where(p >= 0, (p + 1) if w.causal else w.S, 0)
-        flops += 4.0 * w.D * float(n_keys.sum())
-        done += len(rows)
+    for bh in range(w.B * w.H):
+        if t_used >= budget_s:
+            break
+        b, h = divmod(bh, w.H)
+        q, k, v = (gen_slice(w, t, b, h)[None, None].astype(np.float64) for t in "qkv")
+        slices += 1
+        for r0 in range(0, lq, chunk):
+            if t_used >= budget_s:
+                break
+            rows = np.sort(order[r0:r0 + chunk])
+            t0 = time.perf_counter()
+            oracle.rank_reference(q, k, v, w.S, w.cp, lay, rank, w.causal, rows=rows)
+            t_used += time.perf_counter() - t0
+            p = local_pos[rows]
+            n_keys = np.where(p >= 0, (p + 1) if w.causal else w.S, 0)
+            flops += 4.0 * w.D * float(n_keys.sum())
+            rows_done += len(rows)
     return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{done} of {lq} local rows of (b=0, h=0), rank {rank}, fp64 numpy, {t_used:.1f} s"}
+            "sample": f"{rows_done} local rows of rank {rank} over {slices} (b, h) slice(s) "
+                      f"of {w.B * w.H}, fp64 numpy, {t_used:.1f} s of oracle time"}
+
+
+def measure_state_kernels(cpr, torch, B: int, H: int, Lq: int, D: int, out_dtype, stream, reps: int = 10):
+    """HBM throughput of the finalize and merge kernels at the workload's state shape.
+
+    Algorithmic bytes per row: finalize reads O (4D) + m, l (8) and writes O (D*esize) + LSE (4);
+    merge reads two states (8D + 16) and writes one (4D + 8).
+    """
+    rows = B * H * Lq
+    g = torch.Generator(device="cuda").manual_seed(0)
+    o = torch.randn((B, H, Lq, D), device="cuda", generator=g)
+    m = torch.randn((B, H, Lq), device="cuda", generator=g)
+    l = torch.rand((B, H, Lq), device="cuda", generator=g) + 1.0
+    o2, m2, l2 = torch.randn_like(o), torch.randn_like(m), torch.rand_like(l) + 1.0
+    out = torch.empty((B, H, Lq, D), dtype=out_dtype, device="cuda")
+    lse = torch.empty((B, H, Lq), device="cuda")
+    esize = out.element_size()
+    res = {}
+    for name, fn, nbytes in (
+            ("finalize_kernel", lambda: cpr.cp_ring_attn_finalize(o, m, l, out, lse, stream),
+             rows * (4 * D + 8 + D * esize + 4)),
+            ("merge_kernel", lambda: cpr.cp_ring_attn_merge(o, m, l, o2, m2, l2, stream),
+             rows * (8 * D + 16 + 4 * D + 8))):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes_per_launch": nbytes, "kernel_ms": round(ms, 4)}
+    return res
 
 
 def main():
@@ -193,6 +239,8 @@ def main():
                 "kernel": KERNEL_NAME if w.dtype == "bf16" else "attn_f32_kernel",
                 "kernel_ms": round(kernel_ms, 4), "flop_per_launch": flop}
 
+    state_kernels = measure_state_kernels(cpr, torch, w.B, w.H, ri.lq, w.D, tdt, stream)
+
     cpu = None
     if args.cpu_budget > 0:
         cpu = cpu_baseline(w, rank, args.cpu_budget)
@@ -217,6 +265,7 @@ def main():
                    "allowed_pairs_per_bh": pairs, "run_mode": "stepwise" if args.stepwise else "fused",
                    "input_prep_s": round(t_prep, 1)},
         "roofline": roofline,
+        "state_kernels": state_kernels,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
