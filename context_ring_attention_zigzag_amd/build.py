@@ -54,6 +54,13 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if verbose and errs.strip():
         print(errs)
+    # A kernel whose host pass fails leaves an undefined launch stub behind
+    # without a compiler error; refuse such a library here.
+    import ctypes
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}") from e
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

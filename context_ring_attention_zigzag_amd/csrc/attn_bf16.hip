@@ -68,6 +68,22 @@ constexpr float kTau = 8.0f;    // lazy-rescale threshold: probabilities stay be
 constexpr int kXcds = 8;        // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 constexpr int kBN = 64;         // keys per tile
 constexpr int kMaxTiles = 4096; // key tiles classified per segment of a KV block
+#ifndef CPR_QK_PREFETCH
+#define CPR_QK_PREFETCH 3
+#endif
+#ifndef CPR_PV_PREFETCH
+#define CPR_PV_PREFETCH 4
+#endif
+constexpr int kQkPrefetch = CPR_QK_PREFETCH;   // head-dim steps of K fragments in flight
+constexpr int kPvPrefetch = CPR_PV_PREFETCH;   // MFMAs of V fragments in flight
+
+// Fourth dword of a raw buffer descriptor on gfx9-family parts (32-bit data
+// format, no swizzle, no format conversion).
+constexpr int kBufWord3 = 0x00020000;
+
+// scheduling-group masks (AMDGPU sched_group_barrier)
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 template <int D, int NW>
 struct Cfg {
@@ -78,10 +94,10 @@ struct Cfg {
   static constexpr int kChunks = D / 8;            // 16-byte chunks per K/V row
   static constexpr int kDq = D / 32;               // 32-column V sub-blocks per 4-key group
   static constexpr int kTileChunks = kBN * kChunks;
-  static constexpr int kLoadsPerWave = kTileChunks / (64 * NW);   // wave-wide 16-byte loads per tensor
+  static constexpr int kLoadsPerWave = kTileChunks / (64 * (NW / 2));   // per tensor, per loading wave
   static constexpr int kNB = 4 * kDTiles;          // MFMAs of O^T per tile
   static_assert(NW % 2 == 0, "two wave groups");
-  static_assert(kLoadsPerWave >= 1 && kTileChunks % (64 * NW) == 0, "tile/threads mismatch");
+  static_assert(kLoadsPerWave >= 1 && kTileChunks % (64 * (NW / 2)) == 0, "tile/threads mismatch");
 };
 
 // K tile: row-major, physical 16-byte chunk = logical chunk XOR a function of
@@ -121,7 +137,9 @@ __device__ __forceinline__ int wave_max(int x) {
 // first use). The memory clobber keeps the compiler from moving memory
 // accesses across it.
 __device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// vmcnt(0), expcnt and lgkmcnt left at their maximum (gfx9 encoding); the
+// builtin, unlike inline asm, is visible to the compiler's own wait tracking.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int N>
 using ic = std::integral_constant<int, N>;
@@ -149,7 +167,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar registers and branches
   const int group = wave / (NW / 2);   // 0 leads, 1 trails by one phase
   const int ql = lane & 31;   // query column owned by this lane
   const int hh = lane >> 5;   // half-wave
@@ -329,86 +347,123 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       // the global chunk the layout puts there. Rows past Lk re-read row Lk-1
       // (finite data; those keys are masked, so their P is exactly 0). A tile
       // index >= nseg (past the last kept tile) loads nothing.
+      // Each tile load goes through a buffer descriptor whose base is the tile's
+      // first row and whose size covers the rows that exist: rows past Lk read as
+      // zeros (those keys are masked by index, so their P is exactly 0). Buffer
+      // loads keep the compiler's LDS wait counting exact, where global->LDS
+      // loads make it fall back to draining every outstanding LDS read.
       auto issue_k = [&](int j, auto slot, int pslot) __attribute__((always_inline)) {
         if (j >= nseg) return;
         const int r_base = (seg0 + j) * kBN;
+        const uint32_t nrows = (uint32_t)min(kBN, a.Lk - r_base);
+        const uint32_t rs = (uint32_t)a.k_sl * 2u;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (int64_t)r_base * a.k_sl), 0, nrows * rs, kBufWord3);
         __bf16* dst = decltype(slot)::value ? k_lds1 : k_lds0;
+        int ln = lane;
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" : "+v"(ln));   // recompute the lane offsets here instead of keeping them live
+#endif
 #pragma unroll
         for (int u = 0; u < C::kLoadsPerWave; ++u) {
-          const int blk = wave * C::kLoadsPerWave + u;
-          const int s = blk * 64 + lane;
-          const int row = s / C::kChunks;
-          const int lch = swz_k<D>(row, s % C::kChunks);
-          const int grow = min(r_base + row, a.Lk - 1);
-          __builtin_amdgcn_global_load_lds(kb + (int64_t)grow * a.k_sl + lch * 8, (lds_void*)(dst + blk * 512), 16,
-                                           0, 0);
+          const int blk = (wave - NW / 2) * C::kLoadsPerWave + u;
+          const unsigned sidx = (unsigned)(blk * 64 + ln);
+          const int row = (int)(sidx / C::kChunks);
+          const int lch = swz_k<D>(row, (int)(sidx % C::kChunks));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + blk * 512), 16,
+                                                   (uint32_t)row * rs + (uint32_t)lch * 16u, 0, 0, 0);
         }
         if (wave == NW - 1) {
-          const int r = min(r_base + lane, a.Lk - 1);
-          __builtin_amdgcn_global_load_lds(posb + r, (lds_void*)&pos_lds[pslot][0], 4, 0, 0);
+          const __amdgpu_buffer_rsrc_t rp =
+              __builtin_amdgcn_make_buffer_rsrc((void*)(posb + r_base), 0, nrows * 4u, kBufWord3);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void*)&pos_lds[pslot][0], 4, (uint32_t)ln * 4u, 0, 0, 0);
         }
       };
       auto issue_v = [&](int j, auto slot) __attribute__((always_inline)) {
         if (j >= nseg) return;
         const int r_base = (seg0 + j) * kBN;
+        const uint32_t nrows = (uint32_t)min(kBN, a.Lk - r_base);
+        const uint32_t rs = (uint32_t)a.v_sl * 2u;
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(vb + (int64_t)r_base * a.v_sl), 0, nrows * rs, kBufWord3);
         __bf16* dst = decltype(slot)::value ? v_lds1 : v_lds0;
+        int ln = lane;
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" : "+v"(ln));
+#endif
 #pragma unroll
         for (int u = 0; u < C::kLoadsPerWave; ++u) {
-          const int blk = wave * C::kLoadsPerWave + u;
-          const int s = blk * 64 + lane;
-          const int sb = s >> 4, q = s & 15;
-          const int row = 4 * (sb / kDq) + (q >> 2);
-          const int lch = 4 * (sb % kDq) + (q & 3);
-          const int grow = min(r_base + row, a.Lk - 1);
-          __builtin_amdgcn_global_load_lds(vb + (int64_t)grow * a.v_sl + lch * 8, (lds_void*)(dst + blk * 512), 16,
-                                           0, 0);
+          const int blk = (wave - NW / 2) * C::kLoadsPerWave + u;
+          const unsigned sidx = (unsigned)(blk * 64 + ln);
+          const unsigned sb = sidx >> 4, q = sidx & 15;
+          const int row = (int)(4 * (sb / kDq) + (q >> 2));
+          const int lch = (int)(4 * (sb % kDq) + (q & 3));
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + blk * 512), 16,
+                                                   (uint32_t)row * rs + (uint32_t)lch * 16u, 0, 0, 0);
         }
       };
 
       // ---- MFMA phase pieces
-      // S^T = K Q^T for two 32-key sub-tiles; K fragments fetched two steps ahead
+      // S^T = K Q^T for two 32-key sub-tiles. K fragments are fetched kPf head-dim
+      // steps ahead; the read / MFMA order is pinned so that every MFMA waits only
+      // for reads issued kPf steps earlier.
       auto qk = [&](auto slot, f32x16 (&s)[2]) __attribute__((always_inline)) {
+        constexpr int kPf = kQkPrefetch;
         const __bf16* kl = decltype(slot)::value ? k_lds1 : k_lds0;
-        bf16x8 kf[3][2];
+        bf16x8 kf[kPf + 1][2];
         auto fetch = [&](int kk) __attribute__((always_inline)) {
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
-            kf[kk % 3][kt] = *reinterpret_cast<const bf16x8*>(kl + kt * 32 * D + koff[kk]);
+            kf[kk % (kPf + 1)][kt] = *reinterpret_cast<const bf16x8*>(kl + kt * 32 * D + koff[kk]);
         };
-        fetch(0);
-        fetch(1);
+#pragma unroll
+        for (int kk = 0; kk < kPf; ++kk) fetch(kk);
 #pragma unroll
         for (int kk = 0; kk < C::kKSteps; ++kk) {
-          if (kk + 2 < C::kKSteps) fetch(kk + 2);
+          if (kk + kPf < C::kKSteps) fetch(kk + kPf);
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
             if (kk == 0) {
               const f32x16 z = {};
               s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][kt], qf[0], z, 0, 0, 0);
             } else {
-              s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % 3][kt], qf[kk], s[kt], 0, 0, 0);
+              s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % (kPf + 1)][kt], qf[kk], s[kt], 0, 0, 0);
             }
           }
         }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPf, 0);
+#pragma unroll
+        for (int kk = 0; kk < C::kKSteps; ++kk) {
+          if (kk + kPf < C::kKSteps) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        }
       };
-      // O^T += V^T P^T; V fragments (two transposed reads each) fetched two MFMAs ahead
+      // O^T += V^T P^T; V fragments (two transposed reads each) fetched kPf MFMAs
+      // ahead, order pinned as for the scores
       auto pv = [&](auto slot, const bf16x8 (&pb)[4]) __attribute__((always_inline)) {
+        constexpr int kPf = kPvPrefetch;
         const __bf16* vl = decltype(slot)::value ? v_lds1 : v_lds0;
-        s16x4 vf[3][2];
+        s16x4 vf[kPf + 1][2];
         auto fetch = [&](int m) __attribute__((always_inline)) {
           const int ch = m / C::kDTiles, dt = m % C::kDTiles;
           const __bf16* p = vl + vbase + (4 * ch * kDq + dt) * 128;
-          vf[m % 3][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-          vf[m % 3][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2 * kDq * 128));
+          vf[m % (kPf + 1)][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+          vf[m % (kPf + 1)][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2 * kDq * 128));
         };
-        fetch(0);
-        fetch(1);
+#pragma unroll
+        for (int m = 0; m < kPf; ++m) fetch(m);
 #pragma unroll
         for (int m = 0; m < C::kNB; ++m) {
-          if (m + 2 < C::kNB) fetch(m + 2);
+          if (m + kPf < C::kNB) fetch(m + kPf);
           const int ch = m / C::kDTiles, dt = m % C::kDTiles;
-          const s16x8 vv = __builtin_shufflevector(vf[m % 3][0], vf[m % 3][1], 0, 1, 2, 3, 4, 5, 6, 7);
+          const s16x8 vv = __builtin_shufflevector(vf[m % (kPf + 1)][0], vf[m % (kPf + 1)][1], 0, 1, 2, 3, 4, 5, 6, 7);
           ot[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[ch], ot[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPf, 0);
+#pragma unroll
+        for (int m = 0; m < C::kNB; ++m) {
+          if (m + kPf < C::kNB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         }
       };
 
@@ -473,6 +528,28 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         }
       };
 
+      // Empty asm statements that read the given registers: the values must be
+      // computed before this point in program order, which keeps the MFMAs of
+      // an MFMA phase and the exponentials of a VALU phase from drifting across
+      // the phase barrier.
+      // (Vector-register constraints exist only in the device pass.)
+      auto pin_scores = [&](const f32x16 (&x)[2]) __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" ::"v"(x[0]), "v"(x[1]));
+#endif
+      };
+      auto pin_out = [&]() __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt) asm volatile("" ::"v"(ot[dt]));
+#endif
+      };
+      auto pin_probs = [&](const bf16x8 (&x)[4]) __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(lsum0), "v"(lsum1));
+#endif
+      };
+
       // Kept tiles j_0, j_1, ... in order; tile u uses K buffer u&1, V buffer
       // u&1 and position buffer u%3. Global phases: group 0 runs the MFMA phase
       // of tile u in phase 2u and its VALU phase in 2u+1; group 1 runs them in
@@ -489,27 +566,28 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       bf16x8 pb[4];
 
       // prologue: K of tile 0, then tile 0 (no P*V yet)
-      issue_k(ju, ic<0>{}, 0);
+      if (group == 1) issue_k(ju, ic<0>{}, 0);
       wait_vmem();
       bar();
       if (group == 0) {
-        issue_k(ju1, ic<1>{}, 1);
-        issue_v(ju, ic<0>{});
         qk(ic<0>{}, s);
+        pin_scores(s);
         bar();
         softmax(s, pb, ju, 0);
-        wait_vmem();
+        pin_probs(pb);
         bar();
       } else {
         issue_k(ju1, ic<1>{}, 1);
         issue_v(ju, ic<0>{});
         bar();
         qk(ic<0>{}, s);
+        pin_scores(s);
         wait_vmem();
         bar();
         issue_k(ju2, ic<0>{}, 2);
         issue_v(ju1, ic<1>{});
         softmax(s, pb, ju, 0);
+        pin_probs(pb);
         bar();
       }
       ju = ju1;
@@ -521,27 +599,21 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       auto tile = [&](auto kslot) __attribute__((always_inline)) -> bool {
         constexpr int KS = decltype(kslot)::value;   // u & 1
         const bool has = ju < nseg;
-        const int pu1 = mod3_next(pu), pu2 = mod3_next(pu1);
-        if (group == 0) {
-          issue_k(ju1, ic<KS ^ 1>{}, pu1);
-          issue_v(ju, ic<KS>{});
-          pv(ic<KS ^ 1>{}, pb);
-          qk(ic<KS>{}, s);   // stale K when !has: computed, never used
-          bar();
-          if (has) softmax(s, pb, ju, pu);
-          wait_vmem();
-          bar();
-        } else {
-          pv(ic<KS ^ 1>{}, pb);
-          qk(ic<KS>{}, s);
-          wait_vmem();
-          bar();
+        const int pu2 = mod3_next(mod3_next(pu));
+        pv(ic<KS ^ 1>{}, pb);
+        qk(ic<KS>{}, s);   // stale K when !has: computed, never used
+        pin_out();
+        pin_scores(s);
+        if (group == 1) wait_vmem();
+        bar();
+        if (group == 1) {
           issue_k(ju2, ic<KS>{}, pu2);
           issue_v(ju1, ic<KS ^ 1>{});
-          if (has) softmax(s, pb, ju, pu);
-          bar();
         }
-        pu = pu1;
+        if (has) softmax(s, pb, ju, pu);
+        pin_probs(pb);
+        bar();
+        pu = mod3_next(pu);
         ju = ju1;
         ju1 = ju2;
         ju2 = next_kept(ju2);
