@@ -600,9 +600,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         constexpr int KS = decltype(kslot)::value;   // u & 1
         const bool has = ju < nseg;
         const int pu2 = mod3_next(mod3_next(pu));
-        pv(ic<KS ^ 1>{}, pb);
+        // MFMA phase: scores of this tile first (the VALU phase needs them), then
+        // P*V of the previous tile; its last MFMAs may still run when the barrier
+        // passes, since only the LDS reads have to be complete there.
         qk(ic<KS>{}, s);   // stale K when !has: computed, never used
-        pin_out();
+        pv(ic<KS ^ 1>{}, pb);
         pin_scores(s);
         if (group == 1) wait_vmem();
         bar();
@@ -612,11 +614,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         }
         if (has) softmax(s, pb, ju, pu);
         pin_probs(pb);
-        bar();
+        // advance the tile window here, off the MFMA phase's critical path
         pu = mod3_next(pu);
         ju = ju1;
         ju1 = ju2;
         ju2 = next_kept(ju2);
+        bar();
         return has;
       };
       while (true) {
