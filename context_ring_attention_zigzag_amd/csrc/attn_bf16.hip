@@ -68,14 +68,10 @@ constexpr float kTau = 8.0f;    // lazy-rescale threshold: probabilities stay be
 constexpr int kXcds = 8;        // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 constexpr int kBN = 64;         // keys per tile
 constexpr int kMaxTiles = 4096; // key tiles classified per segment of a KV block
-#ifndef CPR_QK_PREFETCH
-#define CPR_QK_PREFETCH 3
+#ifndef CPR_M_PREFETCH
+#define CPR_M_PREFETCH 5
 #endif
-#ifndef CPR_PV_PREFETCH
-#define CPR_PV_PREFETCH 4
-#endif
-constexpr int kQkPrefetch = CPR_QK_PREFETCH;   // head-dim steps of K fragments in flight
-constexpr int kPvPrefetch = CPR_PV_PREFETCH;   // MFMAs of V fragments in flight
+constexpr int kMPrefetch = CPR_M_PREFETCH;   // MFMAs whose LDS operand reads are in flight
 
 // Fourth dword of a raw buffer descriptor on gfx9-family parts (32-bit data
 // format, no swizzle, no format conversion).
@@ -94,10 +90,10 @@ struct Cfg {
   static constexpr int kChunks = D / 8;            // 16-byte chunks per K/V row
   static constexpr int kDq = D / 32;               // 32-column V sub-blocks per 4-key group
   static constexpr int kTileChunks = kBN * kChunks;
-  static constexpr int kLoadsPerWave = kTileChunks / (64 * (NW / 2));   // per tensor, per loading wave
+  static constexpr int kLoadsPerWave = kTileChunks / (64 * NW);   // 16-byte wave loads per tensor and tile
   static constexpr int kNB = 4 * kDTiles;          // MFMAs of O^T per tile
   static_assert(NW % 2 == 0, "two wave groups");
-  static_assert(kLoadsPerWave >= 1 && kTileChunks % (64 * (NW / 2)) == 0, "tile/threads mismatch");
+  static_assert(kLoadsPerWave >= 1 && kTileChunks % (64 * NW) == 0, "tile/threads mismatch");
 };
 
 // K tile: row-major, physical 16-byte chunk = logical chunk XOR a function of
@@ -152,14 +148,16 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   constexpr int kThreads = C::kThreads;
   constexpr int kDq = C::kDq;
 
-  // Separate arrays per K/V buffer so that every MFMA-phase access names its
-  // buffer statically; three position buffers (positions are read one phase
-  // longer than K).
+  // Three K and three V tile buffers, a separate array each so that every
+  // MFMA-phase access names its buffer statically; four position buffers
+  // (positions are read one phase later than K).
   __shared__ __attribute__((aligned(16))) __bf16 k_lds0[kBN * D];
   __shared__ __attribute__((aligned(16))) __bf16 k_lds1[kBN * D];
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds2[kBN * D];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds0[kBN * D];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds1[kBN * D];
-  __shared__ __attribute__((aligned(16))) int32_t pos_lds[3][kBN];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds2[kBN * D];
+  __shared__ __attribute__((aligned(16))) int32_t pos_lds[4][kBN];
   __shared__ uint64_t keep_w[kMaxTiles / 64];
   __shared__ uint64_t mixed_w[kMaxTiles / 64];
   __shared__ uint8_t flags8[kMaxTiles];
@@ -347,122 +345,140 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       // the global chunk the layout puts there. Rows past Lk re-read row Lk-1
       // (finite data; those keys are masked, so their P is exactly 0). A tile
       // index >= nseg (past the last kept tile) loads nothing.
-      // Each tile load goes through a buffer descriptor whose base is the tile's
-      // first row and whose size covers the rows that exist: rows past Lk read as
-      // zeros (those keys are masked by index, so their P is exactly 0). Buffer
-      // loads keep the compiler's LDS wait counting exact, where global->LDS
-      // loads make it fall back to draining every outstanding LDS read.
-      auto issue_k = [&](int j, auto slot, int pslot) __attribute__((always_inline)) {
-        if (j >= nseg) return;
-        const int r_base = (seg0 + j) * kBN;
-        const uint32_t nrows = (uint32_t)min(kBN, a.Lk - r_base);
-        const uint32_t rs = (uint32_t)a.k_sl * 2u;
-        const __amdgpu_buffer_rsrc_t rk =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (int64_t)r_base * a.k_sl), 0, nrows * rs, kBufWord3);
-        __bf16* dst = decltype(slot)::value ? k_lds1 : k_lds0;
-        int ln = lane;
-#if defined(__HIP_DEVICE_COMPILE__)
-        asm volatile("" : "+v"(ln));   // recompute the lane offsets here instead of keeping them live
-#endif
-#pragma unroll
-        for (int u = 0; u < C::kLoadsPerWave; ++u) {
-          const int blk = (wave - NW / 2) * C::kLoadsPerWave + u;
+      auto kbuf = [&](auto slot) __attribute__((always_inline)) -> __bf16* {
+        if constexpr (decltype(slot)::value == 0) return k_lds0;
+        else if constexpr (decltype(slot)::value == 1) return k_lds1;
+        else return k_lds2;
+      };
+      auto vbuf = [&](auto slot) __attribute__((always_inline)) -> __bf16* {
+        if constexpr (decltype(slot)::value == 0) return v_lds0;
+        else if constexpr (decltype(slot)::value == 1) return v_lds1;
+        else return v_lds2;
+      };
+
+      // ---- tile loads. Each goes through a buffer descriptor whose base is the
+      // tile's first row and whose size covers the rows that exist: rows past Lk
+      // read as zeros (those keys are masked by index, so their P is exactly 0),
+      // and a tile index past the last kept tile gets an empty descriptor (the
+      // load only zero-fills a buffer no one reads), so every wave issues the same
+      // number of loads in every MFMA phase. Buffer loads also keep the compiler's
+      // LDS wait counting exact, where global->LDS loads make it drain every
+      // outstanding LDS read.
+      // (three descriptors: K, V and positions; kept as separate values, since
+      // buffer-descriptor values cannot be members of a struct in the host pass)
+      auto make_desc = [&](int jk, int jv, __amdgpu_buffer_rsrc_t& dk, __amdgpu_buffer_rsrc_t& dv,
+                           __amdgpu_buffer_rsrc_t& dp) __attribute__((always_inline)) {
+        {
+          const bool ok = jk < nseg;
+          const int r_base = ok ? (seg0 + jk) * kBN : 0;
+          const uint32_t nrows = ok ? (uint32_t)min(kBN, a.Lk - r_base) : 0u;
+          dk = __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (int64_t)r_base * a.k_sl), 0,
+                                                 nrows * (uint32_t)a.k_sl * 2u, kBufWord3);
+          dp = __builtin_amdgcn_make_buffer_rsrc((void*)(posb + r_base), 0, nrows * 4u, kBufWord3);
+        }
+        {
+          const bool ok = jv < nseg;
+          const int r_base = ok ? (seg0 + jv) * kBN : 0;
+          const uint32_t nrows = ok ? (uint32_t)min(kBN, a.Lk - r_base) : 0u;
+          dv = __builtin_amdgcn_make_buffer_rsrc((void*)(vb + (int64_t)r_base * a.v_sl), 0,
+                                                 nrows * (uint32_t)a.v_sl * 2u, kBufWord3);
+        }
+      };
+      // load number i (0 .. kDmaPerWave-1) of this wave's share: K, then V, then positions
+      auto dma = [&](const __amdgpu_buffer_rsrc_t& dk, const __amdgpu_buffer_rsrc_t& dv,
+                     const __amdgpu_buffer_rsrc_t& dp, int i, int ln, __bf16* kdst, __bf16* vdst, int pslot)
+          __attribute__((always_inline)) {
+        if (i < C::kLoadsPerWave) {
+          const int blk = wave * C::kLoadsPerWave + i;
           const unsigned sidx = (unsigned)(blk * 64 + ln);
           const int row = (int)(sidx / C::kChunks);
           const int lch = swz_k<D>(row, (int)(sidx % C::kChunks));
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(dst + blk * 512), 16,
-                                                   (uint32_t)row * rs + (uint32_t)lch * 16u, 0, 0, 0);
-        }
-        if (wave == NW - 1) {
-          const __amdgpu_buffer_rsrc_t rp =
-              __builtin_amdgcn_make_buffer_rsrc((void*)(posb + r_base), 0, nrows * 4u, kBufWord3);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rp, (lds_void*)&pos_lds[pslot][0], 4, (uint32_t)ln * 4u, 0, 0, 0);
-        }
-      };
-      auto issue_v = [&](int j, auto slot) __attribute__((always_inline)) {
-        if (j >= nseg) return;
-        const int r_base = (seg0 + j) * kBN;
-        const uint32_t nrows = (uint32_t)min(kBN, a.Lk - r_base);
-        const uint32_t rs = (uint32_t)a.v_sl * 2u;
-        const __amdgpu_buffer_rsrc_t rv =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(vb + (int64_t)r_base * a.v_sl), 0, nrows * rs, kBufWord3);
-        __bf16* dst = decltype(slot)::value ? v_lds1 : v_lds0;
-        int ln = lane;
-#if defined(__HIP_DEVICE_COMPILE__)
-        asm volatile("" : "+v"(ln));
-#endif
-#pragma unroll
-        for (int u = 0; u < C::kLoadsPerWave; ++u) {
-          const int blk = (wave - NW / 2) * C::kLoadsPerWave + u;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(dk, (lds_void*)(kdst + blk * 512), 16,
+                                                   (uint32_t)row * (uint32_t)a.k_sl * 2u + (uint32_t)lch * 16u, 0,
+                                                   0, 0);
+        } else if (i < 2 * C::kLoadsPerWave) {
+          const int blk = wave * C::kLoadsPerWave + (i - C::kLoadsPerWave);
           const unsigned sidx = (unsigned)(blk * 64 + ln);
           const unsigned sb = sidx >> 4, q = sidx & 15;
           const int row = (int)(4 * (sb / kDq) + (q >> 2));
           const int lch = (int)(4 * (sb % kDq) + (q & 3));
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)(dst + blk * 512), 16,
-                                                   (uint32_t)row * rs + (uint32_t)lch * 16u, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(dv, (lds_void*)(vdst + blk * 512), 16,
+                                                   (uint32_t)row * (uint32_t)a.v_sl * 2u + (uint32_t)lch * 16u, 0,
+                                                   0, 0);
+        } else if (wave == NW - 1) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(dp, (lds_void*)&pos_lds[pslot][0], 4, (uint32_t)ln * 4u, 0, 0, 0);
         }
+      };
+      constexpr int kDmaPerWave = 2 * C::kLoadsPerWave + 1;   // the last one only on wave NW-1
+      // this wave's share of K and positions of tile jk, V of tile jv
+      auto issue_loads = [&](int jk, int jv, __bf16* kdst, __bf16* vdst, int pslot) __attribute__((always_inline)) {
+        __amdgpu_buffer_rsrc_t dk, dv, dp;
+        make_desc(jk, jv, dk, dv, dp);
+        int ln = lane;
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" : "+v"(ln));   // recompute the load offsets here instead of keeping them live
+#endif
+#pragma unroll
+        for (int i = 0; i < kDmaPerWave; ++i) dma(dk, dv, dp, i, ln, kdst, vdst, pslot);
       };
 
-      // ---- MFMA phase pieces
-      // S^T = K Q^T for two 32-key sub-tiles. K fragments are fetched kPf head-dim
-      // steps ahead; the read / MFMA order is pinned so that every MFMA waits only
-      // for reads issued kPf steps earlier.
-      auto qk = [&](auto slot, f32x16 (&s)[2]) __attribute__((always_inline)) {
-        constexpr int kPf = kQkPrefetch;
-        const __bf16* kl = decltype(slot)::value ? k_lds1 : k_lds0;
-        bf16x8 kf[kPf + 1][2];
-        auto fetch = [&](int kk) __attribute__((always_inline)) {
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt)
-            kf[kk % (kPf + 1)][kt] = *reinterpret_cast<const bf16x8*>(kl + kt * 32 * D + koff[kk]);
-        };
-#pragma unroll
-        for (int kk = 0; kk < kPf; ++kk) fetch(kk);
-#pragma unroll
-        for (int kk = 0; kk < C::kKSteps; ++kk) {
-          if (kk + kPf < C::kKSteps) fetch(kk + kPf);
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            if (kk == 0) {
-              const f32x16 z = {};
-              s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0][kt], qf[0], z, 0, 0, 0);
-            } else {
-              s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kk % (kPf + 1)][kt], qf[kk], s[kt], 0, 0, 0);
-            }
-          }
-        }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPf, 0);
-#pragma unroll
-        for (int kk = 0; kk < C::kKSteps; ++kk) {
-          if (kk + kPf < C::kKSteps) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
-        }
-      };
-      // O^T += V^T P^T; V fragments (two transposed reads each) fetched kPf MFMAs
-      // ahead, order pinned as for the scores
-      auto pv = [&](auto slot, const bf16x8 (&pb)[4]) __attribute__((always_inline)) {
-        constexpr int kPf = kPvPrefetch;
-        const __bf16* vl = decltype(slot)::value ? v_lds1 : v_lds0;
-        s16x4 vf[kPf + 1][2];
+      // ---- MFMA phase: one stream of MFMAs, scores of this tile (S^T = K Q^T,
+      // two 32-key sub-tiles, kNA MFMAs) then O^T += V^T P^T of the previous tile
+      // (kNB MFMAs). Every MFMA's A operand is a 4-register fragment read from LDS
+      // kMPrefetch MFMAs ahead through one ring, across the switch from K to V;
+      // this wave's share of the next tiles' loads is spread over the first
+      // MFMAs. The read / load / MFMA order is pinned with scheduling-group
+      // barriers.
+      auto mphase = [&](auto kslot, auto vslot, auto with_pv, f32x16 (&s)[2], const bf16x8 (&pb)[4])
+          __attribute__((always_inline)) {
+        constexpr int kNA = 2 * C::kKSteps;
+        constexpr int kN = kNA + (decltype(with_pv)::value ? C::kNB : 0);
+        constexpr int kPf = kMPrefetch;
+        const __bf16* kl = kbuf(kslot);
+        const __bf16* vl = vbuf(vslot);
+        bf16x8 fr[kPf + 1];
         auto fetch = [&](int m) __attribute__((always_inline)) {
-          const int ch = m / C::kDTiles, dt = m % C::kDTiles;
-          const __bf16* p = vl + vbase + (4 * ch * kDq + dt) * 128;
-          vf[m % (kPf + 1)][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-          vf[m % (kPf + 1)][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2 * kDq * 128));
+          if (m < kNA) {   // K row 32*kt + ql, logical chunk 2*kk + hh
+            const int kk = m >> 1, kt = m & 1;
+            fr[m % (kPf + 1)] = *reinterpret_cast<const bf16x8*>(kl + kt * 32 * D + koff[kk]);
+          } else {         // V^T fragment through two transposed reads
+            const int mm = m - kNA;
+            const int ch = mm / C::kDTiles, dt = mm % C::kDTiles;
+            const __bf16* p = vl + vbase + (4 * ch * kDq + dt) * 128;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2 * kDq * 128));
+            fr[m % (kPf + 1)] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
         };
 #pragma unroll
         for (int m = 0; m < kPf; ++m) fetch(m);
 #pragma unroll
-        for (int m = 0; m < C::kNB; ++m) {
-          if (m + kPf < C::kNB) fetch(m + kPf);
-          const int ch = m / C::kDTiles, dt = m % C::kDTiles;
-          const s16x8 vv = __builtin_shufflevector(vf[m % (kPf + 1)][0], vf[m % (kPf + 1)][1], 0, 1, 2, 3, 4, 5, 6, 7);
-          ot[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pb[ch], ot[dt], 0, 0, 0);
+        for (int m = 0; m < kN; ++m) {
+          if (m + kPf < kN) fetch(m + kPf);
+          if (m < kNA) {
+            const int kk = m >> 1, kt = m & 1;
+            if (kk == 0) {
+              const f32x16 z = {};
+              s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (kPf + 1)], qf[0], z, 0, 0, 0);
+            } else {
+              s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (kPf + 1)], qf[kk], s[kt], 0, 0, 0);
+            }
+          } else {
+            const int mm = m - kNA;
+            const int ch = mm / C::kDTiles, dt = mm % C::kDTiles;
+            ot[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (kPf + 1)], pb[ch], ot[dt], 0, 0, 0);
+          }
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kPf, 0);
+        // pinned order: the first kPf fetches, then per MFMA: its look-ahead fetch, the MFMA, a load
 #pragma unroll
-        for (int m = 0; m < C::kNB; ++m) {
-          if (m + kPf < C::kNB) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        for (int m = 0; m < kPf; ++m) {
+          if (m < kNA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+          else __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+#pragma unroll
+        for (int m = 0; m < kN; ++m) {
+          if (m + kPf < kNA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+          else if (m + kPf < kN) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         }
       };
@@ -550,13 +566,15 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
 #endif
       };
 
-      // Kept tiles j_0, j_1, ... in order; tile u uses K buffer u&1, V buffer
-      // u&1 and position buffer u%3. Global phases: group 0 runs the MFMA phase
+      // Kept tiles j_0, j_1, ... in order. Tile u uses K buffer u%3, V buffer
+      // u%3 and position buffer u%4. Global phases: group 0 runs the MFMA phase
       // of tile u in phase 2u and its VALU phase in 2u+1; group 1 runs them in
-      // 2u+1 and 2u+2. In phase 2u both groups load K and positions of tile u+1
-      // and V of tile u (group 0 at the start of its MFMA phase of tile u,
-      // group 1 at the start of its VALU phase of tile u-1); each wave waits for
-      // its loads before the barrier that ends phase 2u+1.
+      // 2u+1 and 2u+2. The VALU phase of tile u also loads this wave's share of
+      // K and positions of tile u+2 and V of tile u+1 (the buffers they replace
+      // were last read in phase 2u-1); the wave waits for them at the end of its
+      // next MFMA phase, before the barrier that ends phase 2u+3, and their first
+      // reader runs in phase 2u+4. Loads thus sit in the phases with slack: the
+      // VALU phase is shorter than the MFMA phase it overlaps.
       int ju = next_kept(-1);
       if (ju >= nseg) continue;   // uniform: every wave sees the same bitmask
       int ju1 = next_kept(ju);
@@ -565,57 +583,42 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       f32x16 s[2];
       bf16x8 pb[4];
 
-      // prologue: K of tile 0, then tile 0 (no P*V yet)
-      if (group == 1) issue_k(ju, ic<0>{}, 0);
+      // prologue: K and positions of tiles 0 and 1, V of tile 0
+      issue_loads(ju, ju, k_lds0, v_lds0, 0);
+      issue_loads(ju1, nseg, k_lds1, v_lds2, 1);   // (V part: empty descriptor into an unused buffer)
       wait_vmem();
       bar();
-      if (group == 0) {
-        qk(ic<0>{}, s);
-        pin_scores(s);
-        bar();
-        softmax(s, pb, ju, 0);
-        pin_probs(pb);
-        bar();
-      } else {
-        issue_k(ju1, ic<1>{}, 1);
-        issue_v(ju, ic<0>{});
-        bar();
-        qk(ic<0>{}, s);
-        pin_scores(s);
-        wait_vmem();
-        bar();
-        issue_k(ju2, ic<0>{}, 2);
-        issue_v(ju1, ic<1>{});
-        softmax(s, pb, ju, 0);
-        pin_probs(pb);
-        bar();
-      }
+      if (group == 1) bar();   // group 1 trails by one phase
+
+      // tile 0: no P*V yet
+      mphase(ic<0>{}, ic<2>{}, ic<0>{}, s, pb);
+      pin_scores(s);
+      bar();
+      issue_loads(ju2, ju1, k_lds2, v_lds1, 2);
+      softmax(s, pb, ju, 0);
+      pin_probs(pb);
       ju = ju1;
       ju1 = ju2;
       ju2 = next_kept(ju2);
+      bar();
 
       // tile u >= 1; after the last kept tile one more MFMA phase finishes P*V
-      int pu = 1;   // u % 3
+      int pu = 1;   // u % 4
       auto tile = [&](auto kslot) __attribute__((always_inline)) -> bool {
-        constexpr int KS = decltype(kslot)::value;   // u & 1
+        constexpr int KS = decltype(kslot)::value;   // u % 3
         const bool has = ju < nseg;
-        const int pu2 = mod3_next(mod3_next(pu));
         // MFMA phase: scores of this tile first (the VALU phase needs them), then
         // P*V of the previous tile; its last MFMAs may still run when the barrier
         // passes, since only the LDS reads have to be complete there.
-        qk(ic<KS>{}, s);   // stale K when !has: computed, never used
-        pv(ic<KS ^ 1>{}, pb);
+        mphase(ic<KS>{}, ic<(KS + 2) % 3>{}, ic<1>{}, s, pb);   // stale K when !has: scores never used
         pin_scores(s);
-        if (group == 1) wait_vmem();
+        wait_vmem();   // this wave's loads from its previous VALU phase
         bar();
-        if (group == 1) {
-          issue_k(ju2, ic<KS>{}, pu2);
-          issue_v(ju1, ic<KS ^ 1>{});
-        }
+        issue_loads(ju2, ju1, kbuf(ic<(KS + 2) % 3>{}), vbuf(ic<(KS + 1) % 3>{}), (pu + 2) & 3);
         if (has) softmax(s, pb, ju, pu);
         pin_probs(pb);
         // advance the tile window here, off the MFMA phase's critical path
-        pu = mod3_next(pu);
+        pu = (pu + 1) & 3;
         ju = ju1;
         ju1 = ju2;
         ju2 = next_kept(ju2);
@@ -624,8 +627,10 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       };
       while (true) {
         if (!tile(ic<1>{})) break;
+        if (!tile(ic<2>{})) break;
         if (!tile(ic<0>{})) break;
       }
+      wait_vmem();             // the last phases only zero-filled unused buffers; let them land
       if (group == 0) bar();   // group 1 ran one extra barrier at the start
     }
   }
