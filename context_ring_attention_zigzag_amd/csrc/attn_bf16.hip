@@ -60,7 +60,7 @@ typedef short s16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef short s16x8 __attribute__((__vector_size__(8 * sizeof(short))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -68,6 +68,7 @@ constexpr float kTau = 8.0f;    // lazy-rescale threshold: probabilities stay be
 constexpr int kXcds = 8;        // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 constexpr int kBN = 64;         // keys per tile
 constexpr int kMaxTiles = 4096; // key tiles classified per segment of a KV block
+constexpr int kListPad = 8;     // end markers after the last kept tile (look-ahead reads)
 #ifndef CPR_M_PREFETCH
 #define CPR_M_PREFETCH 5
 #endif
@@ -76,6 +77,42 @@ constexpr int kMPrefetch = CPR_M_PREFETCH;   // MFMAs whose LDS operand reads ar
 // Fourth dword of a raw buffer descriptor on gfx9-family parts (32-bit data
 // format, no swizzle, no format conversion).
 constexpr int kBufWord3 = 0x00020000;
+
+// Raw buffer descriptor (scalar registers): base, no stride, `nbytes` bytes
+// addressable; offsets at or past nbytes read as zero.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = (int)(uint32_t)p;
+  r.y = (int)((uint32_t)(p >> 32) & 0xffffu);
+  r.z = (int)nbytes;
+  r.w = kBufWord3;
+  return r;
+}
+
+// LDS address (byte offset) of a __shared__ object
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr(T* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) T*)p);
+}
+
+// Direct buffer -> LDS loads: lane i of the wave writes its 16 (4) bytes at
+// LDS address m0 + 16*i (4*i). Issued as inline assembly on purpose: the
+// compiler then neither counts them nor inserts waits for them before LDS
+// reads of other tile buffers (it cannot tell the buffers apart), and the
+// kernel waits for them explicitly with vm_wait<N>(), one tile after issue.
+__device__ __forceinline__ void dma_b128(const i32x4& rsrc, uint32_t voff, uint32_t m0) {
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma_b32(const i32x4& rsrc, uint32_t voff, uint32_t m0) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(m0) : "memory");
+}
+// wait until at most N of this wave's vector-memory loads are outstanding
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // scheduling-group masks (AMDGPU sched_group_barrier)
 constexpr int kSchedMfma = 0x008;
@@ -133,14 +170,10 @@ __device__ __forceinline__ int wave_max(int x) {
 // first use). The memory clobber keeps the compiler from moving memory
 // accesses across it.
 __device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// vmcnt(0), expcnt and lgkmcnt left at their maximum (gfx9 encoding); the
-// builtin, unlike inline asm, is visible to the compiler's own wait tracking.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 template <int N>
 using ic = std::integral_constant<int, N>;
 
-__device__ __forceinline__ int mod3_next(int x) { return x == 2 ? 0 : x + 1; }
 
 template <int D, int NW>
 __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
@@ -158,10 +191,10 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 v_lds1[kBN * D];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds2[kBN * D];
   __shared__ __attribute__((aligned(16))) int32_t pos_lds[4][kBN];
-  __shared__ uint64_t keep_w[kMaxTiles / 64];
-  __shared__ uint64_t mixed_w[kMaxTiles / 64];
-  __shared__ uint8_t flags8[kMaxTiles];
+  __shared__ __attribute__((aligned(8))) uint8_t flags8[kMaxTiles];
+  __shared__ uint16_t klist[kMaxTiles + kListPad];
   __shared__ int32_t qrange[2][NW];
+  __shared__ int32_t wcount[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -270,6 +303,21 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   // ((key/4)*kDq + d/32)*128 + (key%4)*32 + d%32.
   const int vbase = (lane >> 5) * kDq * 128 + ((lane & 15) >> 2) * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
 
+  // Per-lane byte offsets of this wave's share of a tile load (loop invariant):
+  // wave load i fills the 16-byte LDS chunks blk*64 + lane, blk = wave*kLoadsPerWave + i,
+  // with the global chunk that the tile layout puts there.
+  uint32_t ldk[C::kLoadsPerWave], ldv[C::kLoadsPerWave];
+#pragma unroll
+  for (int i = 0; i < C::kLoadsPerWave; ++i) {
+    const unsigned sidx = (unsigned)((wave * C::kLoadsPerWave + i) * 64 + lane);
+    const int krow = (int)(sidx / C::kChunks);
+    ldk[i] = (uint32_t)krow * (uint32_t)a.k_sl * 2u + (uint32_t)swz_k<D>(krow, (int)(sidx % C::kChunks)) * 16u;
+    const unsigned sb = sidx >> 4, q = sidx & 15;   // 4-key x 32-column sub-block, chunk within it
+    const unsigned vrow = 4 * (sb / kDq) + (q >> 2), vch = 4 * (sb % kDq) + (q & 3);
+    ldv[i] = vrow * (uint32_t)a.v_sl * 2u + vch * 16u;
+  }
+  const uint32_t ldp = (uint32_t)lane * 4u;
+
   for (int t = 0; t < a.nblocks && wg_has_queries; ++t) {
     int src = (a.rank - t) % a.cp;
     if (src < 0) src += a.cp;
@@ -282,7 +330,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       const int nseg = min(kMaxTiles, n_kt - seg0);
 
       // ---- classify the segment's key tiles: 16 lanes per tile, 4 positions each
-      bar();   // the previous segment is done with flags8 / keep_w / the buffers
+      bar();   // the previous segment is done with flags8 / klist / the buffers
       for (int base = 0; base < nseg; base += kThreads / 16) {
         const int tt = base + (tid >> 4);
         const int g16 = tid & 15;
@@ -315,36 +363,47 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         }
       }
       bar();
-      for (int tt = tid; tt < ((nseg + 63) & ~63); tt += kThreads) {
-        const int f = tt < nseg ? flags8[tt] : 0;
-        const uint64_t kw = __ballot(f & 1);
-        const uint64_t mw = __ballot(f & 2);
-        if (lane == 0) {
-          keep_w[tt >> 6] = kw;
-          mixed_w[tt >> 6] = mw;
+
+      // ---- ordered list of the kept tiles (entry = tile index, | 0x8000 when the
+      // tile needs the element mask), then kListPad end markers equal to nseg.
+      // Thread tid covers tiles [8*tid, 8*tid + 8): count, scan, scatter.
+      int nk;
+      {
+        static_assert(kMaxTiles == 8 * kThreads, "eight tile flags per thread");
+        const int t0 = 8 * tid;
+        uint64_t fw = 0;
+        if (t0 < nseg) {
+          fw = *reinterpret_cast<const uint64_t*>(&flags8[t0]);
+          if (nseg - t0 < 8) fw &= (1ull << (8 * (nseg - t0))) - 1ull;
         }
+        const int cnt = __builtin_popcountll(fw & 0x0101010101010101ull);
+        int incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int y = __shfl_up(incl, o);
+          incl += lane >= o ? y : 0;
+        }
+        if (lane == 63) wcount[wave] = incl;
+        bar();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const int c = wcount[w];
+          before += w < wave ? c : 0;
+          total += c;
+        }
+        int p = before + incl - cnt;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int f = (int)(fw >> (8 * e)) & 3;
+          if (f & 1) klist[p++] = (uint16_t)((t0 + e) | ((f & 2) ? 0x8000 : 0));
+        }
+        if (tid < kListPad) klist[total + tid] = (uint16_t)nseg;
+        nk = __builtin_amdgcn_readfirstlane(total);
       }
       bar();
+      if (nk == 0) continue;   // uniform
 
-      const int nwords = (nseg + 63) >> 6;
-      auto next_kept = [&](int j) __attribute__((always_inline)) -> int {   // first kept tile index > j, or nseg
-        if (j >= nseg) return nseg;
-        int w = (j + 1) >> 6;
-        if (w >= nwords) return nseg;
-        uint64_t bits = keep_w[w] & (~0ull << ((j + 1) & 63));
-        while (bits == 0) {
-          if (++w >= nwords) return nseg;
-          bits = keep_w[w];
-        }
-        return __builtin_amdgcn_readfirstlane(min(nseg, (w << 6) + (int)__builtin_ctzll(bits)));
-      };
-      auto is_mixed = [&](int j) __attribute__((always_inline)) -> bool { return (mixed_w[j >> 6] >> (j & 63)) & 1ull; };
-
-      // ---- direct global -> LDS loads (this wave's share of a tile): lane
-      // `lane` of wave-load `blk` fills the 16-byte LDS chunk blk*64 + lane with
-      // the global chunk the layout puts there. Rows past Lk re-read row Lk-1
-      // (finite data; those keys are masked, so their P is exactly 0). A tile
-      // index >= nseg (past the last kept tile) loads nothing.
       auto kbuf = [&](auto slot) __attribute__((always_inline)) -> __bf16* {
         if constexpr (decltype(slot)::value == 0) return k_lds0;
         else if constexpr (decltype(slot)::value == 1) return k_lds1;
@@ -356,79 +415,50 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         else return v_lds2;
       };
 
-      // ---- tile loads. Each goes through a buffer descriptor whose base is the
-      // tile's first row and whose size covers the rows that exist: rows past Lk
-      // read as zeros (those keys are masked by index, so their P is exactly 0),
-      // and a tile index past the last kept tile gets an empty descriptor (the
-      // load only zero-fills a buffer no one reads), so every wave issues the same
-      // number of loads in every MFMA phase. Buffer loads also keep the compiler's
-      // LDS wait counting exact, where global->LDS loads make it drain every
-      // outstanding LDS read.
-      // (three descriptors: K, V and positions; kept as separate values, since
-      // buffer-descriptor values cannot be members of a struct in the host pass)
-      auto make_desc = [&](int jk, int jv, __amdgpu_buffer_rsrc_t& dk, __amdgpu_buffer_rsrc_t& dv,
-                           __amdgpu_buffer_rsrc_t& dp) __attribute__((always_inline)) {
-        {
-          const bool ok = jk < nseg;
-          const int r_base = ok ? (seg0 + jk) * kBN : 0;
-          const uint32_t nrows = ok ? (uint32_t)min(kBN, a.Lk - r_base) : 0u;
-          dk = __builtin_amdgcn_make_buffer_rsrc((void*)(kb + (int64_t)r_base * a.k_sl), 0,
-                                                 nrows * (uint32_t)a.k_sl * 2u, kBufWord3);
-          dp = __builtin_amdgcn_make_buffer_rsrc((void*)(posb + r_base), 0, nrows * 4u, kBufWord3);
-        }
-        {
-          const bool ok = jv < nseg;
-          const int r_base = ok ? (seg0 + jv) * kBN : 0;
-          const uint32_t nrows = ok ? (uint32_t)min(kBN, a.Lk - r_base) : 0u;
-          dv = __builtin_amdgcn_make_buffer_rsrc((void*)(vb + (int64_t)r_base * a.v_sl), 0,
-                                                 nrows * (uint32_t)a.v_sl * 2u, kBufWord3);
-        }
+      // ---- tile loads, this wave's share. Each goes through a buffer descriptor
+      // whose base is the tile's first row and whose size covers the rows that
+      // exist: rows past Lk read as zeros (those keys are masked by index, so their
+      // P is exactly 0), and a tile index >= nseg (an end marker) gets an empty
+      // descriptor, whose loads only zero-fill a buffer no one reads; every wave
+      // thus issues the same loads in every VALU phase.
+      auto tile_rows = [&](int j) __attribute__((always_inline)) -> uint32_t {
+        return j < nseg ? (uint32_t)min(kBN, a.Lk - (seg0 + j) * kBN) : 0u;
       };
-      // load number i (0 .. kDmaPerWave-1) of this wave's share: K, then V, then positions
-      auto dma = [&](const __amdgpu_buffer_rsrc_t& dk, const __amdgpu_buffer_rsrc_t& dv,
-                     const __amdgpu_buffer_rsrc_t& dp, int i, int ln, __bf16* kdst, __bf16* vdst, int pslot)
-          __attribute__((always_inline)) {
-        if (i < C::kLoadsPerWave) {
-          const int blk = wave * C::kLoadsPerWave + i;
-          const unsigned sidx = (unsigned)(blk * 64 + ln);
-          const int row = (int)(sidx / C::kChunks);
-          const int lch = swz_k<D>(row, (int)(sidx % C::kChunks));
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(dk, (lds_void*)(kdst + blk * 512), 16,
-                                                   (uint32_t)row * (uint32_t)a.k_sl * 2u + (uint32_t)lch * 16u, 0,
-                                                   0, 0);
-        } else if (i < 2 * C::kLoadsPerWave) {
-          const int blk = wave * C::kLoadsPerWave + (i - C::kLoadsPerWave);
-          const unsigned sidx = (unsigned)(blk * 64 + ln);
-          const unsigned sb = sidx >> 4, q = sidx & 15;
-          const int row = (int)(4 * (sb / kDq) + (q >> 2));
-          const int lch = (int)(4 * (sb % kDq) + (q & 3));
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(dv, (lds_void*)(vdst + blk * 512), 16,
-                                                   (uint32_t)row * (uint32_t)a.v_sl * 2u + (uint32_t)lch * 16u, 0,
-                                                   0, 0);
-        } else if (wave == NW - 1) {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(dp, (lds_void*)&pos_lds[pslot][0], 4, (uint32_t)ln * 4u, 0, 0, 0);
-        }
+      auto load_k = [&](int j, auto i, __bf16* dst) __attribute__((always_inline)) {
+        const int r0 = j < nseg ? (seg0 + j) * kBN : 0;
+        const i32x4 d = make_rsrc(kb + (int64_t)r0 * a.k_sl, tile_rows(j) * (uint32_t)a.k_sl * 2u);
+        dma_b128(d, ldk[decltype(i)::value], lds_addr(dst + (wave * C::kLoadsPerWave + decltype(i)::value) * 512));
       };
-      constexpr int kDmaPerWave = 2 * C::kLoadsPerWave + 1;   // the last one only on wave NW-1
-      // this wave's share of K and positions of tile jk, V of tile jv
-      auto issue_loads = [&](int jk, int jv, __bf16* kdst, __bf16* vdst, int pslot) __attribute__((always_inline)) {
-        __amdgpu_buffer_rsrc_t dk, dv, dp;
-        make_desc(jk, jv, dk, dv, dp);
-        int ln = lane;
-#if defined(__HIP_DEVICE_COMPILE__)
-        asm volatile("" : "+v"(ln));   // recompute the load offsets here instead of keeping them live
-#endif
-#pragma unroll
-        for (int i = 0; i < kDmaPerWave; ++i) dma(dk, dv, dp, i, ln, kdst, vdst, pslot);
+      auto load_v = [&](int j, auto i, __bf16* dst) __attribute__((always_inline)) {
+        const int r0 = j < nseg ? (seg0 + j) * kBN : 0;
+        const i32x4 d = make_rsrc(vb + (int64_t)r0 * a.v_sl, tile_rows(j) * (uint32_t)a.v_sl * 2u);
+        dma_b128(d, ldv[decltype(i)::value], lds_addr(dst + (wave * C::kLoadsPerWave + decltype(i)::value) * 512));
+      };
+      auto load_pos = [&](int j, int slot) __attribute__((always_inline)) {
+        const int r0 = j < nseg ? (seg0 + j) * kBN : 0;
+        dma_b32(make_rsrc(posb + r0, tile_rows(j) * 4u), ldp, lds_addr(&pos_lds[slot][0]));
+      };
+      // load number n of a VALU phase: K chunks first, then V chunks
+      auto load_nth = [&](auto n, int jk, int jv, __bf16* kd, __bf16* vd) __attribute__((always_inline)) {
+        constexpr int N = decltype(n)::value;
+        if constexpr (N < C::kLoadsPerWave) load_k(jk, ic<N>{}, kd);
+        else load_v(jv, ic<N - C::kLoadsPerWave>{}, vd);
+      };
+      auto load_tile_k = [&](int j, __bf16* dst) __attribute__((always_inline)) {
+        if constexpr (C::kLoadsPerWave >= 1) load_k(j, ic<0>{}, dst);
+        if constexpr (C::kLoadsPerWave >= 2) load_k(j, ic<1>{}, dst);
+        static_assert(C::kLoadsPerWave <= 2, "loads per wave");
+      };
+      auto load_tile_v = [&](int j, __bf16* dst) __attribute__((always_inline)) {
+        if constexpr (C::kLoadsPerWave >= 1) load_v(j, ic<0>{}, dst);
+        if constexpr (C::kLoadsPerWave >= 2) load_v(j, ic<1>{}, dst);
       };
 
       // ---- MFMA phase: one stream of MFMAs, scores of this tile (S^T = K Q^T,
       // two 32-key sub-tiles, kNA MFMAs) then O^T += V^T P^T of the previous tile
       // (kNB MFMAs). Every MFMA's A operand is a 4-register fragment read from LDS
-      // kMPrefetch MFMAs ahead through one ring, across the switch from K to V;
-      // this wave's share of the next tiles' loads is spread over the first
-      // MFMAs. The read / load / MFMA order is pinned with scheduling-group
-      // barriers.
+      // kMPrefetch MFMAs ahead through one ring, across the switch from K to V.
+      // The read / MFMA order is pinned with scheduling-group barriers.
       auto mphase = [&](auto kslot, auto vslot, auto with_pv, f32x16 (&s)[2], const bf16x8 (&pb)[4])
           __attribute__((always_inline)) {
         constexpr int kNA = 2 * C::kKSteps;
@@ -469,7 +499,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
             ot[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (kPf + 1)], pb[ch], ot[dt], 0, 0, 0);
           }
         }
-        // pinned order: the first kPf fetches, then per MFMA: its look-ahead fetch, the MFMA, a load
+        // pinned order: the first kPf fetches, then per MFMA: its look-ahead fetch, the MFMA
 #pragma unroll
         for (int m = 0; m < kPf; ++m) {
           if (m < kNA) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
@@ -483,13 +513,13 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         }
       };
 
-      // ---- VALU phase: mask, max, rescale, exponentials, row sums
-      auto softmax = [&](f32x16 (&s)[2], bf16x8 (&pb)[4], int j, int pslot) __attribute__((always_inline)) {
-        if (is_mixed(j)) {
+      // ---- VALU phase, first part: mask, max, rescale decision
+      auto softmax_max = [&](f32x16 (&s)[2], int e, int pslot) __attribute__((always_inline)) {
+        if (e & 0x8000) {
           // element mask of a tile straddling the causal boundary or holding
           // pads / rows past Lk
           const int32_t* pl = &pos_lds[pslot][0];
-          const int rem = a.Lk - (seg0 + j) * kBN;   // keys of this tile that exist
+          const int rem = a.Lk - (seg0 + (e & 0x7fff)) * kBN;   // keys of this tile that exist
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -526,38 +556,44 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
           m_ref = m_new;
           m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
         }
-        // P = 2^(s*c2 - m_ref) rounded to bf16, in the B-operand layout of
-        // O^T += V^T P^T (16 keys per chunk); l accumulates the same values
+      };
+      // ---- VALU phase, second part, 16 keys at a time: P = 2^(s*c2 - m_ref)
+      // rounded to bf16, in the B-operand layout of O^T += V^T P^T; l accumulates
+      // the same values before rounding
+      auto softmax_exp = [&](const f32x16 (&s)[2], bf16x8 (&pb)[4], auto chunk, float mu) __attribute__((always_inline)) {
+        constexpr int c = decltype(chunk)::value;
+        uint32_t w4[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint32_t w4[4];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const float e0 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + 2 * x], c2, -m_use));
-            const float e1 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + 2 * x + 1], c2, -m_use));
-            const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-            lsum0 += e0;
-            lsum1 += e1;
-            w4[x] = __builtin_bit_cast(uint32_t, pr);
-          }
-          pb[c] = __builtin_bit_cast(bf16x8, w4);
+        for (int x = 0; x < 4; ++x) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + 2 * x], c2, -mu));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + 2 * x + 1], c2, -mu));
+          const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
+          lsum0 += e0;
+          lsum1 += e1;
+          w4[x] = __builtin_bit_cast(uint32_t, pr);
         }
+        pb[c] = __builtin_bit_cast(bf16x8, w4);
       };
 
       // Empty asm statements that read the given registers: the values must be
       // computed before this point in program order, which keeps the MFMAs of
       // an MFMA phase and the exponentials of a VALU phase from drifting across
-      // the phase barrier.
+      // the phase barrier, and spaces the loads between the exponentials.
       // (Vector-register constraints exist only in the device pass.)
       auto pin_scores = [&](const f32x16 (&x)[2]) __attribute__((always_inline)) {
 #if defined(__HIP_DEVICE_COMPILE__)
         asm volatile("" ::"v"(x[0]), "v"(x[1]));
 #endif
       };
-      auto pin_out = [&]() __attribute__((always_inline)) {
+      auto pin_chunk = [&](const bf16x8& x) __attribute__((always_inline)) {
 #if defined(__HIP_DEVICE_COMPILE__)
-#pragma unroll
-        for (int dt = 0; dt < C::kDTiles; ++dt) asm volatile("" ::"v"(ot[dt]));
+        asm volatile("" ::"v"(x));
+#endif
+      };
+      // (an empty asm statement that may change x: what uses x afterwards stays after it)
+      auto after_here = [&](float& x) __attribute__((always_inline)) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        asm volatile("" : "+v"(x));
 #endif
       };
       auto pin_probs = [&](const bf16x8 (&x)[4]) __attribute__((always_inline)) {
@@ -566,27 +602,92 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
 #endif
       };
 
-      // Kept tiles j_0, j_1, ... in order. Tile u uses K buffer u%3, V buffer
-      // u%3 and position buffer u%4. Global phases: group 0 runs the MFMA phase
-      // of tile u in phase 2u and its VALU phase in 2u+1; group 1 runs them in
-      // 2u+1 and 2u+2. The VALU phase of tile u also loads this wave's share of
-      // K and positions of tile u+2 and V of tile u+1 (the buffers they replace
-      // were last read in phase 2u-1); the wave waits for them at the end of its
-      // next MFMA phase, before the barrier that ends phase 2u+3, and their first
-      // reader runs in phase 2u+4. Loads thus sit in the phases with slack: the
-      // VALU phase is shorter than the MFMA phase it overlaps.
-      int ju = next_kept(-1);
-      if (ju >= nseg) continue;   // uniform: every wave sees the same bitmask
-      int ju1 = next_kept(ju);
-      int ju2 = next_kept(ju1);
+      // Kept tiles 0, 1, ... of the list in order; tile u uses K buffer u%3, V
+      // buffer u%3 and position buffer u%4. Global phases: group 0 runs the MFMA
+      // phase of tile u in phase 2u and its VALU phase in 2u+1; group 1 runs them
+      // in 2u+1 and 2u+2. In its VALU phase of tile u a wave of group 0 loads its
+      // share of K of tile u+2 and V of tile u+1, a wave of group 1 its share of K
+      // of tile u+3 and V of tile u+2 (wave NW-1 also the positions of tile u+3):
+      // each buffer is free by then (its last readers ran before the preceding
+      // barrier), and each wave waits for its loads at the end of its next VALU
+      // phase, one barrier before the first reader of the data. The list entries
+      // of tiles u .. u+3 ride in e0 .. e3.
+      int u = 0;
+      int e0 = __builtin_amdgcn_readfirstlane((int)klist[0]);
+      int e1 = __builtin_amdgcn_readfirstlane((int)klist[1]);
+      int e2 = __builtin_amdgcn_readfirstlane((int)klist[2]);
+      int e3 = __builtin_amdgcn_readfirstlane((int)klist[3]);
+      auto tix = [](int e) __attribute__((always_inline)) { return e & 0x7fff; };
 
       f32x16 s[2];
       bf16x8 pb[4];
 
-      // prologue: K and positions of tiles 0 and 1, V of tile 0
-      issue_loads(ju, ju, k_lds0, v_lds0, 0);
-      issue_loads(ju1, nseg, k_lds1, v_lds2, 1);   // (V part: empty descriptor into an unused buffer)
-      wait_vmem();
+      auto vphase = [&](auto kslot, bool has) __attribute__((always_inline)) {
+        constexpr int KS = decltype(kslot)::value;   // u % 3
+        constexpr int kL = C::kLoadsPerWave;
+        const int ahead = klist[u + 4];              // read now, used at the end
+        __bf16* kd = group == 0 ? kbuf(ic<(KS + 2) % 3>{}) : kbuf(ic<KS>{});
+        __bf16* vd = group == 0 ? vbuf(ic<(KS + 1) % 3>{}) : vbuf(ic<(KS + 2) % 3>{});
+        const int jk = tix(group == 0 ? e2 : e3);
+        const int jv = tix(group == 0 ? e1 : e2);
+        if (has) {
+          // load n goes out between exponential chunks n-1 and n (pinned in
+          // program order), so the loads of the four waves of a group reach the
+          // memory pipeline spread over the phase instead of queueing at its start
+          float mu;
+          load_nth(ic<0>{}, jk, jv, kd, vd);
+          softmax_max(s, e0, u & 3);
+          mu = m_use;
+          softmax_exp(s, pb, ic<0>{}, mu);
+          pin_chunk(pb[0]);
+          load_nth(ic<1>{}, jk, jv, kd, vd);
+          after_here(mu);
+          softmax_exp(s, pb, ic<1>{}, mu);
+          if constexpr (2 * kL > 2) {
+            pin_chunk(pb[1]);
+            load_nth(ic<2>{}, jk, jv, kd, vd);
+            after_here(mu);
+          }
+          softmax_exp(s, pb, ic<2>{}, mu);
+          if constexpr (2 * kL > 3) {
+            pin_chunk(pb[2]);
+            load_nth(ic<3>{}, jk, jv, kd, vd);
+            after_here(mu);
+          }
+          softmax_exp(s, pb, ic<3>{}, mu);
+        } else {
+          load_tile_k(jk, kd);
+          load_tile_v(jv, vd);
+        }
+        if (wave == NW - 1) load_pos(tix(e3), (u + 3) & 3);
+        pin_probs(pb);
+        // the loads of the previous VALU phase have landed
+        if (wave == NW - 1) vm_wait<2 * kL + 1>();
+        else vm_wait<2 * kL>();
+        e0 = e1;
+        e1 = e2;
+        e2 = e3;
+        e3 = __builtin_amdgcn_readfirstlane(ahead);
+        ++u;
+        bar();
+      };
+
+      // prologue: K of tiles 0 and 1, V of tile 0, positions of tiles 0 .. 2;
+      // group 1, which loads one tile further ahead, also its share of K of tile 2
+      // and V of tile 1
+      load_tile_k(tix(e0), k_lds0);
+      load_tile_k(tix(e1), k_lds1);
+      load_tile_v(tix(e0), v_lds0);
+      if (group == 1) {
+        load_tile_k(tix(e2), k_lds2);
+        load_tile_v(tix(e1), v_lds1);
+      }
+      if (wave == NW - 1) {
+        load_pos(tix(e0), 0);
+        load_pos(tix(e1), 1);
+        load_pos(tix(e2), 2);
+      }
+      vm_wait<0>();
       bar();
       if (group == 1) bar();   // group 1 trails by one phase
 
@@ -594,35 +695,19 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       mphase(ic<0>{}, ic<2>{}, ic<0>{}, s, pb);
       pin_scores(s);
       bar();
-      issue_loads(ju2, ju1, k_lds2, v_lds1, 2);
-      softmax(s, pb, ju, 0);
-      pin_probs(pb);
-      ju = ju1;
-      ju1 = ju2;
-      ju2 = next_kept(ju2);
-      bar();
+      vphase(ic<0>{}, true);
 
       // tile u >= 1; after the last kept tile one more MFMA phase finishes P*V
-      int pu = 1;   // u % 4
       auto tile = [&](auto kslot) __attribute__((always_inline)) -> bool {
         constexpr int KS = decltype(kslot)::value;   // u % 3
-        const bool has = ju < nseg;
-        // MFMA phase: scores of this tile first (the VALU phase needs them), then
-        // P*V of the previous tile; its last MFMAs may still run when the barrier
-        // passes, since only the LDS reads have to be complete there.
+        const bool has = tix(e0) < nseg;
+        // scores of this tile first (the VALU phase needs them), then P*V of the
+        // previous tile; its last MFMAs may still run when the barrier passes,
+        // since only the LDS reads have to be complete there
         mphase(ic<KS>{}, ic<(KS + 2) % 3>{}, ic<1>{}, s, pb);   // stale K when !has: scores never used
         pin_scores(s);
-        wait_vmem();   // this wave's loads from its previous VALU phase
         bar();
-        issue_loads(ju2, ju1, kbuf(ic<(KS + 2) % 3>{}), vbuf(ic<(KS + 1) % 3>{}), (pu + 2) & 3);
-        if (has) softmax(s, pb, ju, pu);
-        pin_probs(pb);
-        // advance the tile window here, off the MFMA phase's critical path
-        pu = (pu + 1) & 3;
-        ju = ju1;
-        ju1 = ju2;
-        ju2 = next_kept(ju2);
-        bar();
+        vphase(kslot, has);
         return has;
       };
       while (true) {
@@ -630,7 +715,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         if (!tile(ic<2>{})) break;
         if (!tile(ic<0>{})) break;
       }
-      wait_vmem();             // the last phases only zero-filled unused buffers; let them land
+      vm_wait<0>();            // the last phases only zero-filled unused buffers; let them land
       if (group == 0) bar();   // group 1 ran one extra barrier at the start
     }
   }
