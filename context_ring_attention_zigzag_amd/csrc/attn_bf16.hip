@@ -514,32 +514,43 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       };
 
       // ---- VALU phase, first part: mask, max, rescale decision
-      auto softmax_max = [&](f32x16 (&s)[2], int e, int pslot) __attribute__((always_inline)) {
+      // the row max of a tile's scores over this half-wave's keys
+      auto row_max = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) -> float {
+        float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          m0 = fmaxf(m0, s[0][i]);
+          m1 = fmaxf(m1, s[1][i]);
+        }
+        return fmaxf(m0, m1);
+      };
+      // mxh: row max of the unmasked scores, taken in the MFMA phase
+      auto softmax_max = [&](f32x16 (&s)[2], int e, int pslot, float mxh) __attribute__((always_inline)) {
         if (e & 0x8000) {
           // element mask of a tile straddling the causal boundary or holding
-          // pads / rows past Lk
-          const int32_t* pl = &pos_lds[pslot][0];
-          const int rem = a.Lk - (seg0 + (e & 0x7fff)) * kBN;   // keys of this tile that exist
+          // pads / rows past Lk; the row max is taken again over what is left
+          const int32_t* pl = &pos_lds[pslot][4 * hh];
+          // keys of this tile that exist, less this half-wave's key offset: key
+          // kt*32 + 8*i + 4*hh + jj exists when kt*32 + 8*i + jj < remh
+          const int remh = a.Lk - (seg0 + (e & 0x7fff)) * kBN - 4 * hh;
+          // the causal test pk <= qp becomes pk <= qlim; qlim = INT_MAX when not
+          // causal, -1 for a pad query (which then matches no key: pk >= 0 fails)
+          const int qlim = qp < 0 ? -1 : (a.causal ? qp : INT_MAX);
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int key0 = kt * 32 + 8 * i + 4 * hh;
-              const int4 p = *reinterpret_cast<const int4*>(pl + key0);
+              const int4 p = *reinterpret_cast<const int4*>(pl + kt * 32 + 8 * i);
               const int pk[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
               for (int jj = 0; jj < 4; ++jj) {
-                const bool ok = key0 + jj < rem && pk[jj] >= 0 && qp >= 0 && (!a.causal || pk[jj] <= qp);
+                const bool ok = kt * 32 + 8 * i + jj < remh && pk[jj] >= 0 && pk[jj] <= qlim;
                 s[kt][4 * i + jj] = ok ? s[kt][4 * i + jj] : -INFINITY;
               }
             }
+          mxh = row_max(s);
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
-        mx = other_half_max(mx);
+        const float mx = other_half_max(mxh);
         // raise the reference max where this tile's max outgrew it by more than kTau
         const float mt = mx * c2;
         m_true = fmaxf(m_true, mt);
@@ -580,9 +591,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       // an MFMA phase and the exponentials of a VALU phase from drifting across
       // the phase barrier, and spaces the loads between the exponentials.
       // (Vector-register constraints exist only in the device pass.)
-      auto pin_scores = [&](const f32x16 (&x)[2]) __attribute__((always_inline)) {
+      auto pin_scores = [&](const f32x16 (&x)[2], const float& m) __attribute__((always_inline)) {
 #if defined(__HIP_DEVICE_COMPILE__)
-        asm volatile("" ::"v"(x[0]), "v"(x[1]));
+        asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(m));
 #endif
       };
       auto pin_chunk = [&](const bf16x8& x) __attribute__((always_inline)) {
@@ -622,7 +633,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       f32x16 s[2];
       bf16x8 pb[4];
 
-      auto vphase = [&](auto kslot, bool has) __attribute__((always_inline)) {
+      auto vphase = [&](auto kslot, bool has, float mxh) __attribute__((always_inline)) {
         constexpr int KS = decltype(kslot)::value;   // u % 3
         constexpr int kL = C::kLoadsPerWave;
         const int ahead = klist[u + 4];              // read now, used at the end
@@ -636,7 +647,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
           // memory pipeline spread over the phase instead of queueing at its start
           float mu;
           load_nth(ic<0>{}, jk, jv, kd, vd);
-          softmax_max(s, e0, u & 3);
+          softmax_max(s, e0, u & 3, mxh);
           mu = m_use;
           softmax_exp(s, pb, ic<0>{}, mu);
           pin_chunk(pb[0]);
@@ -693,9 +704,10 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
 
       // tile 0: no P*V yet
       mphase(ic<0>{}, ic<2>{}, ic<0>{}, s, pb);
-      pin_scores(s);
+      float mxh = row_max(s);
+      pin_scores(s, mxh);
       bar();
-      vphase(ic<0>{}, true);
+      vphase(ic<0>{}, true, mxh);
 
       // tile u >= 1; after the last kept tile one more MFMA phase finishes P*V
       auto tile = [&](auto kslot) __attribute__((always_inline)) -> bool {
@@ -705,9 +717,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         // previous tile; its last MFMAs may still run when the barrier passes,
         // since only the LDS reads have to be complete there
         mphase(ic<KS>{}, ic<(KS + 2) % 3>{}, ic<1>{}, s, pb);   // stale K when !has: scores never used
-        pin_scores(s);
+        // the row max of the new scores, beside the P*V MFMAs of this phase
+        mxh = row_max(s);
+        pin_scores(s, mxh);
         bar();
-        vphase(kslot, has);
+        vphase(kslot, has, mxh);
         return has;
       };
       while (true) {
