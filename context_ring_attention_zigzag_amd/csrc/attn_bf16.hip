@@ -14,14 +14,16 @@
 //    of them and keeps their Q rows in VGPRs for the whole pass;
 //  * two wave groups (waves [0, NW/2) and [NW/2, NW), one wave of each per
 //    SIMD) run the same key-tile sequence one phase apart. Each tile takes two
-//    phases: an MFMA phase (P*V of the previous tile, then S^T = K Q^T of this
-//    one) and a VALU phase (mask, row max, exponentials, row sums). While one
+//    phases: an MFMA phase (S^T = K Q^T of this tile, then P*V of the previous
+//    one, with the row max of the new scores beside it) and a VALU phase
+//    (mask, rescale decision, exponentials, row sums, tile loads). While one
 //    group is in its MFMA phase the other is in its VALU phase, so the matrix
 //    cores and the vector ALUs of every SIMD work at the same time; a
 //    workgroup barrier separates consecutive phases;
-//  * keys stream through LDS in tiles of BN = 64 with direct global->LDS
-//    16-byte loads (global_load_lds_dwordx4), issued two phases before their
-//    first use into double-buffered K and V tiles;
+//  * keys stream through LDS in tiles of BN = 64 with direct buffer->LDS
+//    16-byte loads, into three K and three V buffers; every wave waits for its
+//    own loads one tile after issuing them, one barrier before their first
+//    reader;
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: lane l then holds query l%32 and 16 of the 32
 //    keys of a 32x32 block, so the per-query max and sum are lane-local plus
@@ -41,8 +43,9 @@
 //    V is stored as 4-key x 32-column sub-blocks that a 32-lane transposed read
 //    covers without bank conflicts;
 //  * (query tile, key tile) pairs are classified from their position ranges
-//    into skip / full / mixed; skipped tiles are neither loaded nor computed,
-//    full tiles need no element mask;
+//    into skip / full / mixed and the kept ones listed in order in LDS;
+//    skipped tiles are neither loaded nor computed, full tiles need no element
+//    mask;
 //  * the grid is remapped so that the workgroups of one (b, h) land on the
 //    same XCD (shared L2), heaviest query tiles first.
 #include <math.h>
