@@ -77,7 +77,7 @@ def cpu_baseline(w, rank: int, budget_s: float):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    lay = oracle.ZIGZAG if w.layout == "zigzag" else oracle.CONTIGUOUS
+    lay = {"zigzag": oracle.ZIGZAG, "contiguous": oracle.CONTIGUOUS, "striped": oracle.STRIPED}[w.layout]
     tok, pos = oracle.layout(w.S, w.cp, lay)
     lq = len(tok) // w.cp
     local_pos = pos[rank * lq:(rank + 1) * lq]
@@ -142,6 +142,56 @@ def measure_state_kernels(cpr, torch, B: int, H: int, Lq: int, D: int, out_dtype
     return res
 
 
+def layout_balance(args, cpr, di, torch, np, w, gen_slice, lay_codes):
+    """Per-rank time of the fused ring pass for each layout at one causal workload shape.
+
+    The causal split is what the layouts are about: a contiguous split leaves
+    the later ranks with more allowed pairs ("Context Parallelism v.s. Sequence
+    Parallelism (Megatron-LM)", "Implementation quirk: symmetric chunk
+    assignment"); zigzag and striped assignment even them out ("Sequence
+    Parallelism and Ring Attention", "The future of sequence parallelism and
+    ring attention"). Every rank is emulated on this one GPU, one after another.
+    """
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    nat = {t: di.upload(lambda b, h, t=t: gen_slice(w, t, b, h), w.B, w.H, w.S, w.D, tdt) for t in "qkv"}
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name in ("contiguous", "zigzag", "striped"):
+        lay = lay_codes[name]
+        tok, pos = di.layout_arrays(w.S, w.cp, lay)
+        per_rank = []
+        for rank in range(w.cp):
+            ri = di.prepare_rank(nat["q"], nat["k"], nat["v"], w.S, w.cp, lay, rank, tok, pos)
+            o = torch.empty_like(ri.q_local)
+            lse = torch.empty(ri.q_local.shape[:3], dtype=torch.float32, device="cuda")
+            pairs = allowed_pairs(w, ri.s_pad, ri.lq, ri.q_pos.cpu().numpy(), ri.ring_pos.cpu().numpy())
+
+            def run():
+                cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, True, 0.0,
+                                     o, lse, None, cpr.RUN_FUSED, stream)
+            for _ in range(args.warmup):
+                run()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            flop = 4.0 * w.B * w.H * w.D * pairs
+            per_rank.append({"rank": rank, "ms": round(ms, 4), "pairs_per_bh": pairs,
+                             "tflops": round(flop / (ms * 1e-3) / 1e12, 1)})
+            del ri, o, lse
+        slowest = max(p["ms"] for p in per_rank)
+        out[name] = {"per_rank": per_rank, "slowest_ms": slowest,
+                     "slowest_over_mean": round(slowest / (sum(p["ms"] for p in per_rank) / len(per_rank)), 3)}
+    print(json.dumps({"layout_balance": out,
+                      "config": {"B": w.B, "H": w.H, "D": w.D, "seq_len": w.S, "cp_size": w.cp, "causal": True,
+                                 "dtype": w.dtype, "steps": args.steps, "warmup": args.warmup},
+                      "data": "synthetic: seeded N(0,1) draws per (tensor, b, h) slice"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +201,9 @@ def main():
     ap.add_argument("--rank", type=int, default=None)
     ap.add_argument("--stepwise", action="store_true", help="time the init/step/finalize path instead of the fused one")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
+    ap.add_argument("--layout-balance", action="store_true",
+                    help="time every rank of the 32k-token causal sequence under the contiguous, zigzag and striped "
+                         "layouts (one JSON line) instead of the default measurement")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -181,9 +234,14 @@ def main():
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}))
         return
 
+    LAY_CODES = {"zigzag": cpr.ZIGZAG, "contiguous": cpr.CONTIGUOUS, "striped": cpr.STRIPED}
+    if args.layout_balance:
+        layout_balance(args, cpr, di, torch, np, WORKLOADS["seq32k_cp4"], gen_slice, LAY_CODES)
+        return
+
     w = WORKLOADS[args.workload]
     rank = w.ranks[0] if args.rank is None else args.rank
-    lay = cpr.ZIGZAG if w.layout == "zigzag" else cpr.CONTIGUOUS
+    lay = LAY_CODES[w.layout]
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
     t_prep = time.perf_counter()

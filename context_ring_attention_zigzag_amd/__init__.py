@@ -22,7 +22,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libcpring.so")
 
 F32, BF16 = 0, 1
-ZIGZAG, CONTIGUOUS = 0, 1
+ZIGZAG, CONTIGUOUS, STRIPED = 0, 1, 2
 RUN_FUSED, RUN_STEPWISE = 0, 1
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 

@@ -99,7 +99,7 @@ extern "C" {
 
 int64_t cp_padded_len(int64_t seq_len, int32_t cp_size, int32_t layout) {
   if (seq_len < 1 || seq_len > CPR_MAX_SEQ || cp_size < 1) return -1;
-  if (layout != CPR_ZIGZAG && layout != CPR_CONTIGUOUS) return -1;
+  if (layout != CPR_ZIGZAG && layout != CPR_CONTIGUOUS && layout != CPR_STRIPED) return -1;
   const int64_t unit = layout == CPR_ZIGZAG ? 2 * (int64_t)cp_size : (int64_t)cp_size;
   const int64_t s_pad = (seq_len + unit - 1) / unit * unit;
   return s_pad > CPR_MAX_SEQ ? -1 : s_pad;
@@ -108,7 +108,8 @@ int64_t cp_padded_len(int64_t seq_len, int32_t cp_size, int32_t layout) {
 cpr_status cp_zigzag_partition(int64_t seq_len, int32_t cp_size, int32_t layout, int32_t* token_idx,
                                int32_t* pos_ids, void* stream) {
   if (cp_size < 1) return fail(CPR_EINVAL, "cp_size must be >= 1 (got %d)", cp_size);
-  if (layout != CPR_ZIGZAG && layout != CPR_CONTIGUOUS) return fail(CPR_EINVAL, "unknown layout %d", layout);
+  if (layout != CPR_ZIGZAG && layout != CPR_CONTIGUOUS && layout != CPR_STRIPED)
+    return fail(CPR_EINVAL, "unknown layout %d", layout);
   TRY(check_len("seq_len", seq_len));
   const int64_t s_pad = cp_padded_len(seq_len, cp_size, layout);
   if (s_pad < 0) return fail(CPR_EUNSUPPORTED, "padded length exceeds 2^30");

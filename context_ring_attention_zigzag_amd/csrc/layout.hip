@@ -6,6 +6,11 @@
 // the sequence is padded to a multiple of 2*cp.
 // Contiguous: "Sequence Parallelism and Ring Attention", "Deep dive" - rank r
 // holds one contiguous run of tokens.
+// Striped: the same page, "The future of sequence parallelism and ring
+// attention", names striped assignment beside zigzag as the way to even out
+// causal work; the plain reading, taken here, deals token t to rank t mod cp,
+// so rank r holds tokens r, r+cp, r+2cp, ... (the sequence padded to a
+// multiple of cp).
 #include "common.h"
 
 namespace cpring {
@@ -26,6 +31,8 @@ __global__ void __launch_bounds__(256) partition_kernel(int32_t* __restrict__ to
     const bool front = i < c;
     const int32_t chunk = front ? r : 2 * cp - 1 - r;
     tok = chunk * c + (front ? i : i - c);
+  } else if (layout == CPR_STRIPED) {
+    tok = i * cp + r;
   } else {
     tok = k;
   }

@@ -68,7 +68,8 @@ typedef enum { CPR_F32 = 0, CPR_BF16 = 1 } cpr_dtype;
 
 typedef enum {
   CPR_ZIGZAG = 0,     /* rank r: chunks r and 2cp-1-r of 2cp chunks */
-  CPR_CONTIGUOUS = 1  /* rank r: tokens [r*L/cp, (r+1)*L/cp) */
+  CPR_CONTIGUOUS = 1, /* rank r: tokens [r*L/cp, (r+1)*L/cp) */
+  CPR_STRIPED = 2     /* rank r: tokens r, r+cp, r+2cp, ... */
 } cpr_layout;
 
 /* Flags for cp_ring_attn_run. */
@@ -92,7 +93,9 @@ typedef struct cpr_view {
  * Padded sequence length for `seq_len` tokens over `cp_size` ranks: the next
  * multiple of 2*cp_size for CPR_ZIGZAG (Megatron page, symmetric chunk
  * assignment: the sequence must split into 2*cp equal chunks), of cp_size for
- * CPR_CONTIGUOUS ("Sequence Parallelism and Ring Attention", "Deep dive").
+ * CPR_CONTIGUOUS ("Sequence Parallelism and Ring Attention", "Deep dive") and
+ * CPR_STRIPED (the same page, "The future of sequence parallelism and ring
+ * attention": striped assignment, the other way to even out causal work).
  * Returns -1 for seq_len < 1 or > CPR_MAX_SEQ, cp_size < 1, or an unknown layout.
  */
 int64_t cp_padded_len(int64_t seq_len, int32_t cp_size, int32_t layout);
@@ -101,7 +104,8 @@ int64_t cp_padded_len(int64_t seq_len, int32_t cp_size, int32_t layout);
  * Token and position-id layout of all ranks, rank-major: entry r*Lr + i
  * (Lr = S_pad/cp_size) describes the i-th local token of rank r.
  *   token_idx[k]  index of that token in the padded natural order
- *                 (zigzag: chunk r then chunk 2cp-1-r, each in order);
+ *                 (zigzag: chunk r then chunk 2cp-1-r, each in order;
+ *                 contiguous: r*Lr + i; striped: i*cp_size + r);
  *   pos_ids[k]    its global position, or -1 for a pad token (>= seq_len).
  * Both are int32 device arrays of cp_padded_len(...) entries; either may be
  * NULL (not both). Cited: Megatron page, symmetric chunk assignment (chunk

@@ -13,7 +13,8 @@ Pages this oracle follows (cited by title and section):
   (orangingq.tistory.com), sections "Context Parallelism (CP)" and
   "Implementation quirk: symmetric chunk assignment".
 * "Sequence Parallelism and Ring Attention" (aiunderstanding.org), sections
-  "Deep dive", "Technical insight" and the FAQ.
+  "Deep dive", "Technical insight", "The future of sequence parallelism and
+  ring attention" (striped layout) and the FAQ.
 
 Every function here is pinned by ``tests/test_oracle.py`` to something other
 than itself (brute force, a library routine, closed forms, the pages' cp=4
@@ -22,8 +23,10 @@ table). No function is "parity unpinned".
 
 from .ring_attention import (  # noqa: F401
     CONTIGUOUS,
+    STRIPED,
     ZIGZAG,
     allowed_mask,
+    causal_pairs_striped,
     causal_pairs_zigzag,
     count_pairs,
     finalize,

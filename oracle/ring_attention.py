@@ -30,12 +30,16 @@ import numpy as np
 
 ZIGZAG = 0
 CONTIGUOUS = 1
+STRIPED = 2
 
 
 # ---------------------------------------------------------------------------
 # Layout: "Context Parallelism v.s. Sequence Parallelism (Megatron-LM)",
-# section "Implementation quirk: symmetric chunk assignment" (zigzag), and
-# "Sequence Parallelism and Ring Attention", section "Deep dive" (contiguous).
+# section "Implementation quirk: symmetric chunk assignment" (zigzag),
+# "Sequence Parallelism and Ring Attention", section "Deep dive" (contiguous),
+# and the same page's "The future of sequence parallelism and ring attention"
+# (striped, named there beside zigzag as a rebalancing of causal work; read
+# here as token t on rank t mod cp).
 # ---------------------------------------------------------------------------
 
 def padded_len(seq_len: int, cp: int, lay: int) -> int:
@@ -45,7 +49,7 @@ def padded_len(seq_len: int, cp: int, lay: int) -> int:
     to a multiple of 2*cp (Megatron page, symmetric chunk assignment). The
     contiguous split only needs cp equal pieces.
     """
-    if seq_len < 0 or cp < 1 or lay not in (ZIGZAG, CONTIGUOUS):
+    if seq_len < 0 or cp < 1 or lay not in (ZIGZAG, CONTIGUOUS, STRIPED):
         raise ValueError("bad layout arguments")
     unit = 2 * cp if lay == ZIGZAG else cp
     return ((seq_len + unit - 1) // unit) * unit
@@ -61,6 +65,7 @@ def layout(seq_len: int, cp: int, lay: int):
     rank r holds chunk r followed by chunk 2*cp-1-r (the page's cp=4 table:
     rank 0 has chunks 0 and 7, ..., rank 3 has chunks 3 and 4).
     Contiguous: rank r holds tokens [r*Lr, (r+1)*Lr).
+    Striped: token t goes to rank t mod cp, so rank r holds r, r+cp, r+2cp, ...
     pos_ids is the global position of the token, or -1 for a pad token (the
     page insists local positions are the global ones, never 0, 1, 2, ...).
     """
@@ -73,6 +78,9 @@ def layout(seq_len: int, cp: int, lay: int):
             front, back = r, 2 * cp - 1 - r
             token_idx[r * lr: r * lr + c] = np.arange(front * c, front * c + c)
             token_idx[r * lr + c: (r + 1) * lr] = np.arange(back * c, back * c + c)
+    elif lay == STRIPED:
+        for r in range(cp):
+            token_idx[r * lr: (r + 1) * lr] = np.arange(r, s_pad, cp)
     else:
         token_idx[:] = np.arange(s_pad)
     pos_ids = np.where(token_idx < seq_len, token_idx, -1)
@@ -290,6 +298,17 @@ def ring_emulation(q_local, k_ring, v_ring, q_pos, ring_pos, cp: int, rank: int,
 def count_pairs(q_pos, k_pos, causal: bool) -> int:
     """Brute-force number of allowed (query, key) pairs."""
     return int(allowed_mask(q_pos, k_pos, causal).sum())
+
+
+def causal_pairs_striped(s_pad: int, cp: int, rank: int) -> int:
+    """Allowed causal pairs for one rank under the striped layout, no padding.
+
+    Local query i of rank r sits at position i*cp + r and sees the keys at
+    positions 0 .. i*cp + r, i.e. i*cp + r + 1 of them; summed over the
+    Lr = s_pad/cp local queries: cp*Lr*(Lr-1)/2 + Lr*(r+1).
+    """
+    lr = s_pad // cp
+    return cp * lr * (lr - 1) // 2 + lr * (rank + 1)
 
 
 def causal_pairs_zigzag(s_pad: int, cp: int) -> int:

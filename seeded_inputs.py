@@ -30,7 +30,7 @@ class Workload:
     D: int
     S: int              # unpadded sequence length (all ranks together)
     cp: int             # context-parallel size
-    layout: str         # "zigzag" or "contiguous"
+    layout: str         # "zigzag", "contiguous" or "striped"
     ranks: tuple        # ranks emulated on the one GPU
     causal: bool
     input_scale: float  # N(0,1) draws are multiplied by this
@@ -48,6 +48,10 @@ WORKLOADS = {
     "longdoc_noncausal": Workload("longdoc_noncausal", "bf16", 2, 16, 128, 65536, 8, "contiguous", (0,),
                                   False, 0.5, 4),
     "million_cp8": Workload("million_cp8", "bf16", 1, 8, 128, 1048576, 8, "zigzag", (0,), True, 1.0, 5),
+    # the 32k-token sequence again under the striped layout (a layout variant,
+    # not one of the five workloads)
+    "seq32k_cp4_striped": Workload("seq32k_cp4_striped", "bf16", 1, 32, 128, 32768, 4, "striped", (3,), True, 1.0,
+                                   6),
 }
 
 

@@ -52,6 +52,9 @@ def test_padded_len(lib):
     assert lib.cp_padded_len(65536, 8, cpr.CONTIGUOUS) == 65536
     assert lib.cp_padded_len(10, 4, cpr.CONTIGUOUS) == 12
     assert lib.cp_padded_len(1048576, 8, cpr.ZIGZAG) == 1048576
+    assert lib.cp_padded_len(10, 4, cpr.STRIPED) == 12
+    assert lib.cp_padded_len(32768, 4, cpr.STRIPED) == 32768
+    assert lib.cp_padded_len(10, 4, 3) == -1
     for bad in ((0, 2, 0), (-5, 2, 0), (10, 0, 0), (10, 2, 5), (1 << 31, 2, 0)):
         assert lib.cp_padded_len(*bad) == -1
 
@@ -60,7 +63,7 @@ def test_padded_len_matches_oracle(lib):
     import oracle
     for s in (1, 3, 17, 64, 100, 257, 4096):
         for cp in (1, 2, 3, 4, 8):
-            for lay in (cpr.ZIGZAG, cpr.CONTIGUOUS):
+            for lay in (cpr.ZIGZAG, cpr.CONTIGUOUS, cpr.STRIPED):
                 assert lib.cp_padded_len(s, cp, lay) == oracle.padded_len(s, cp, lay)
 
 

@@ -38,8 +38,12 @@ def note(msg):
     print(f"[gpu-parity] {msg}", flush=True)
 
 
+LAY_CODES = {"zigzag": cpr.ZIGZAG, "contiguous": cpr.CONTIGUOUS, "striped": cpr.STRIPED}
+ORACLE_LAYS = {"zigzag": oracle.ZIGZAG, "contiguous": oracle.CONTIGUOUS, "striped": oracle.STRIPED}
+
+
 def lay_code(w):
-    return cpr.ZIGZAG if w.layout == "zigzag" else cpr.CONTIGUOUS
+    return LAY_CODES[w.layout]
 
 
 def compare(o, lse, ro, rl, dtype, what):
@@ -80,7 +84,7 @@ def run_rank(w, dev, rank, flags):
 @pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("s", [1, 5, 64, 100, 257, 4096, 32768])
 def test_partition_bit_exact(cp, s):
-    for lay in (cpr.ZIGZAG, cpr.CONTIGUOUS):
+    for lay in (cpr.ZIGZAG, cpr.CONTIGUOUS, cpr.STRIPED):
         tok, pos = di.layout_arrays(s, cp, lay)
         rt, rp = oracle.layout(s, cp, lay)
         assert np.array_equal(tok.cpu().numpy(), rt.astype(np.int32))
@@ -149,6 +153,10 @@ RAGGED = [
     ("f32", 128, 300, 2, "contiguous", False),
     ("f32", 64, 201, 3, "zigzag", True),
     ("f32", 128, 10, 4, "zigzag", True),        # every rank mostly padding
+    ("bf16", 128, 1000, 4, "striped", True),    # striped: every block holds part of the diagonal
+    ("bf16", 64, 77, 3, "striped", True),       # striped with two pad tokens
+    ("f32", 64, 201, 3, "striped", True),
+    ("bf16", 128, 513, 2, "striped", False),
 ]
 
 
@@ -257,7 +265,7 @@ def sampled_check(name, flags=cpr.RUN_FUSED, n_rows=None):
     """Run the workload's rank(s) on the GPU; compare sampled rows with the oracle head by head."""
     w = WORKLOADS[name]
     lay = lay_code(w)
-    olay = oracle.ZIGZAG if w.layout == "zigzag" else oracle.CONTIGUOUS
+    olay = ORACLE_LAYS[w.layout]
     s_pad = oracle.padded_len(w.S, w.cp, olay)
     lq = s_pad // w.cp
     chunk = lq // 2 if w.layout == "zigzag" else lq
@@ -284,6 +292,10 @@ def sampled_check(name, flags=cpr.RUN_FUSED, n_rows=None):
 
 def test_seq32k_cp4_sampled():
     sampled_check("seq32k_cp4", cpr.RUN_FUSED)
+
+
+def test_seq32k_cp4_striped_sampled():
+    sampled_check("seq32k_cp4_striped", cpr.RUN_FUSED, n_rows=64)
 
 
 def test_seq32k_cp4_stepwise_sampled():

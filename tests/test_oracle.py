@@ -20,7 +20,8 @@ import oracle
 from oracle import ring_attention as ora
 from seeded_inputs import WORKLOADS, gen_tensor, small_workload
 
-ZZ, CT = oracle.ZIGZAG, oracle.CONTIGUOUS
+ZZ, CT, ST = oracle.ZIGZAG, oracle.CONTIGUOUS, oracle.STRIPED
+LAYOUTS = {"zigzag": ZZ, "contiguous": CT, "striped": ST}
 
 
 def rnd(shape, seed, scale=1.0):
@@ -47,7 +48,7 @@ def test_layout_matches_pages_cp4_table(golden_dir):
 @pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
 @pytest.mark.parametrize("s", [1, 7, 16, 33, 64, 100, 257])
 def test_layout_properties(cp, s):
-    for lay in (ZZ, CT):
+    for lay in (ZZ, CT, ST):
         tok, pos = oracle.layout(s, cp, lay)
         s_pad = len(tok)
         unit = 2 * cp if lay == ZZ else cp
@@ -63,8 +64,21 @@ def test_layout_properties(cp, s):
                 # two runs of c consecutive tokens: chunk r, then chunk 2cp-1-r
                 assert local[:c].tolist() == list(range(r * c, r * c + c))
                 assert local[c:].tolist() == list(range((2 * cp - 1 - r) * c, (2 * cp - r) * c))
+            elif lay == ST:
+                # every cp-th token, starting at r
+                assert local.tolist() == list(range(r, s_pad, cp))
             else:
                 assert local.tolist() == list(range(r * lr, (r + 1) * lr))
+
+
+def test_striped_layout_small_examples():
+    """Token t on rank t mod cp, written out by hand for two small cases."""
+    tok, pos = oracle.layout(8, 2, ST)
+    assert tok.tolist() == [0, 2, 4, 6, 1, 3, 5, 7]
+    assert pos.tolist() == [0, 2, 4, 6, 1, 3, 5, 7]
+    tok, pos = oracle.layout(10, 4, ST)   # padded to 12: tokens 10 and 11 are pads
+    assert tok.tolist() == [0, 4, 8, 1, 5, 9, 2, 6, 10, 3, 7, 11]
+    assert pos.tolist() == [0, 4, 8, 1, 5, 9, 2, 6, -1, 3, 7, -1]
 
 
 def test_padded_len_rejects_bad_args():
@@ -180,7 +194,7 @@ def test_closed_form_constant_values_and_dominant_key():
 
 def ring_inputs(w):
     q, k, v = (gen_tensor(w, t).astype(np.float64) for t in "qkv")
-    lay = ZZ if w.layout == "zigzag" else CT
+    lay = LAYOUTS[w.layout]
     tok, pos = oracle.layout(w.S, w.cp, lay)
     s_pad = len(tok)
 
@@ -193,7 +207,7 @@ def ring_inputs(w):
 
 
 @pytest.mark.parametrize("cp", [1, 2, 4, 8])
-@pytest.mark.parametrize("layout", ["zigzag", "contiguous"])
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous", "striped"])
 @pytest.mark.parametrize("causal", [True, False])
 def test_ring_emulation_equals_full_attention(cp, layout, causal):
     w = small_workload("t", "f32", 1, 2, 8, 53, cp, layout, causal, seed=cp * 10 + causal)
@@ -300,6 +314,19 @@ def test_zigzag_balance_closed_form(cp, c):
     counts = [oracle.count_pairs(pos[r * lr:(r + 1) * lr], pos, True) for r in range(cp)]
     assert counts == [oracle.causal_pairs_zigzag(s, cp)] * cp
     assert sum(counts) == s * (s + 1) // 2
+
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("lr", [1, 2, 5, 16])
+def test_striped_pairs_closed_form(cp, lr):
+    """Brute-force per-rank causal pair counts under striping == cp*Lr*(Lr-1)/2 + Lr*(r+1)."""
+    s = cp * lr
+    _, pos = oracle.layout(s, cp, ST)
+    counts = [oracle.count_pairs(pos[r * lr:(r + 1) * lr], pos, True) for r in range(cp)]
+    assert counts == [oracle.causal_pairs_striped(s, cp, r) for r in range(cp)]
+    assert sum(counts) == s * (s + 1) // 2
+    # ranks differ by at most Lr*(cp-1) pairs: nearly even, unlike the contiguous split
+    assert max(counts) - min(counts) == lr * (cp - 1)
 
 
 def test_contiguous_causal_is_imbalanced():
