@@ -30,7 +30,7 @@ OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 EXPORTS = (
     "cp_padded_len", "cp_zigzag_partition", "cp_shard_gather", "cp_ring_attn_init", "cp_ring_attn_step",
     "cp_ring_attn_merge", "cp_ring_attn_finalize", "cp_ring_attn_workspace_size", "cp_ring_attn_run",
-    "cp_status_string", "cp_last_error",
+    "cp_ring_attn_step_ex", "cp_ring_attn_run_ex", "cp_status_string", "cp_last_error",
 )
 
 
@@ -43,6 +43,11 @@ class CprError(RuntimeError):
 class CprView(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_int64), ("stride_h", ctypes.c_int64),
                 ("stride_l", ctypes.c_int64)]
+
+
+class CprAttnExt(ctypes.Structure):
+    """cpr_attn_ext: K/V head count and optional per-query key-position window."""
+    _fields_ = [("H_kv", ctypes.c_int32), ("kw_lo", ctypes.c_void_p), ("kw_hi", ctypes.c_void_p)]
 
 
 _lib = None
@@ -58,6 +63,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
     pv = ctypes.POINTER(CprView)
+    pe = ctypes.POINTER(CprAttnExt)
     sig = {
         "cp_padded_len": (i64, [i64, i32, i32]),
         "cp_zigzag_partition": (i32, [i64, i32, i32, vp, vp, vp]),
@@ -69,6 +75,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "cp_ring_attn_workspace_size": (ctypes.c_size_t, [i32, i32, i32, i32]),
         "cp_ring_attn_run": (i32, [i32, i32, i32, i32, i32, i32, pv, i32, vp, pv, pv, vp, i32, f32, vp, vp, vp,
                                    ctypes.c_size_t, i32, vp]),
+        "cp_ring_attn_step_ex": (i32, [i32, i32, i32, i32, pv, i32, vp, pv, pv, i32, vp, i32, f32, pe, vp, vp, vp,
+                                       vp]),
+        "cp_ring_attn_run_ex": (i32, [i32, i32, i32, i32, i32, i32, pv, i32, vp, pv, pv, vp, i32, f32, pe, vp, vp,
+                                      vp, ctypes.c_size_t, i32, vp]),
         "cp_status_string": (ctypes.c_char_p, [i32]),
         "cp_last_error": (ctypes.c_char_p, []),
     }
@@ -134,13 +144,25 @@ def cp_ring_attn_init(o_acc, m, l, stream=None):
            "cp_ring_attn_init")
 
 
-def cp_ring_attn_step(q, q_pos, k, v, kv_pos, causal: bool, softmax_scale: float, o_acc, m, l, stream=None):
+def _ext(q, k, kw_lo, kw_hi):
+    """cpr_attn_ext for K/V with k.shape[1] heads and the optional windows, or None for the plain pass."""
+    h, h_kv = q.shape[1], k.shape[1]
+    if h_kv == h and kw_lo is None and kw_hi is None:
+        return None
+    return CprAttnExt(h_kv, None if kw_lo is None else kw_lo.data_ptr(), None if kw_hi is None else kw_hi.data_ptr())
+
+
+def cp_ring_attn_step(q, q_pos, k, v, kv_pos, causal: bool, softmax_scale: float, o_acc, m, l, stream=None,
+                      kw_lo=None, kw_hi=None):
+    """One ring step; k and v may have fewer heads than q (grouped-query attention)."""
     B, H, Lq, D = q.shape
     qv, kv, vv = view(q), view(k), view(v)
-    _check(load().cp_ring_attn_step(dtype_code(q), B, H, D, ctypes.byref(qv), Lq, _ptr(q_pos), ctypes.byref(kv),
-                                    ctypes.byref(vv), k.shape[2], _ptr(kv_pos), int(bool(causal)),
-                                    float(softmax_scale), _ptr(o_acc), _ptr(m), _ptr(l), _stream(stream)),
-           "cp_ring_attn_step")
+    ext = _ext(q, k, kw_lo, kw_hi)
+    _check(load().cp_ring_attn_step_ex(dtype_code(q), B, H, D, ctypes.byref(qv), Lq, _ptr(q_pos), ctypes.byref(kv),
+                                       ctypes.byref(vv), k.shape[2], _ptr(kv_pos), int(bool(causal)),
+                                       float(softmax_scale), None if ext is None else ctypes.byref(ext), _ptr(o_acc),
+                                       _ptr(m), _ptr(l), _stream(stream)),
+           "cp_ring_attn_step_ex")
 
 
 def cp_ring_attn_merge(o_acc, m, l, o2, m2, l2, stream=None):
@@ -161,11 +183,21 @@ def cp_ring_attn_workspace_size(B: int, H: int, Lq: int, D: int) -> int:
 
 def cp_ring_attn_run(q_local, q_pos, k_ring, v_ring, ring_pos, cp_size: int, rank: int, causal: bool,
                      softmax_scale: float, o_out, lse_out=None, workspace=None, flags: int = RUN_FUSED,
-                     stream=None):
+                     stream=None, kw_lo=None, kw_hi=None):
+    """One rank's ring pass; k_ring and v_ring may have fewer heads than q_local (grouped-query
+    attention), and kw_lo / kw_hi (int32 [Lq] or None) bound the key positions each query may attend."""
     B, H, Lq, D = q_local.shape
     qv, kv, vv = view(q_local), view(k_ring), view(v_ring)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().cp_ring_attn_run(dtype_code(q_local), B, H, D, cp_size, rank, ctypes.byref(qv), Lq, _ptr(q_pos),
-                                   ctypes.byref(kv), ctypes.byref(vv), _ptr(ring_pos), int(bool(causal)),
-                                   float(softmax_scale), _ptr(o_out), _ptr(lse_out), _ptr(workspace), ws_bytes,
-                                   flags, _stream(stream)), "cp_ring_attn_run")
+    ext = _ext(q_local, k_ring, kw_lo, kw_hi)
+    if ext is None:
+        _check(load().cp_ring_attn_run(dtype_code(q_local), B, H, D, cp_size, rank, ctypes.byref(qv), Lq,
+                                       _ptr(q_pos), ctypes.byref(kv), ctypes.byref(vv), _ptr(ring_pos),
+                                       int(bool(causal)), float(softmax_scale), _ptr(o_out), _ptr(lse_out),
+                                       _ptr(workspace), ws_bytes, flags, _stream(stream)), "cp_ring_attn_run")
+        return
+    _check(load().cp_ring_attn_run_ex(dtype_code(q_local), B, H, D, cp_size, rank, ctypes.byref(qv), Lq,
+                                      _ptr(q_pos), ctypes.byref(kv), ctypes.byref(vv), _ptr(ring_pos),
+                                      int(bool(causal)), float(softmax_scale), ctypes.byref(ext), _ptr(o_out),
+                                      _ptr(lse_out), _ptr(workspace), ws_bytes, flags, _stream(stream)),
+           "cp_ring_attn_run_ex")

@@ -151,8 +151,14 @@ cpr_status cp_ring_attn_init(int32_t B, int32_t H, int32_t Lq, int32_t D, float*
 
 static cpr_status validate_attn(int32_t dtype, int32_t B, int32_t H, int32_t D, const cpr_view* q, int32_t Lq,
                                 const int32_t* q_pos, const cpr_view* k, const cpr_view* v, int64_t Lk_total,
-                                const int32_t* kv_pos) {
+                                const int32_t* kv_pos, const cpr_attn_ext* ext) {
   TRY(check_dims(dtype, B, H, D));
+  if (ext) {
+    if (ext->H_kv < 0 || (ext->H_kv > 0 && H % ext->H_kv != 0))
+      return fail(CPR_EINVAL, "H_kv = %d must be 0 or divide H = %d", ext->H_kv, H);
+    if ((ext->kw_lo && !aligned(ext->kw_lo, 4)) || (ext->kw_hi && !aligned(ext->kw_hi, 4)))
+      return fail(CPR_EINVAL, "key-window arrays must be 4-byte aligned");
+  }
   TRY(check_len("Lq", Lq));
   TRY(check_len("KV length", Lk_total));
   TRY(check_view("q", q, dtype));
@@ -165,7 +171,7 @@ static cpr_status validate_attn(int32_t dtype, int32_t B, int32_t H, int32_t D, 
 
 static AttnArgs make_args(int32_t dtype, int32_t B, int32_t H, int32_t D, const cpr_view* q, int32_t Lq,
                           const int32_t* q_pos, const cpr_view* k, const cpr_view* v, int32_t Lk,
-                          const int32_t* kv_pos, int32_t causal, float softmax_scale) {
+                          const int32_t* kv_pos, int32_t causal, float softmax_scale, const cpr_attn_ext* ext) {
   (void)dtype;
   AttnArgs a{};
   a.q = q->data; a.q_sb = q->stride_b; a.q_sh = q->stride_h; a.q_sl = q->stride_l;
@@ -174,6 +180,9 @@ static AttnArgs make_args(int32_t dtype, int32_t B, int32_t H, int32_t D, const 
   a.v = v->data; a.v_sb = v->stride_b; a.v_sh = v->stride_h; a.v_sl = v->stride_l;
   a.kv_pos = kv_pos;
   a.B = B; a.H = H; a.D = D; a.Lq = Lq; a.Lk = Lk;
+  a.H_kv = (ext && ext->H_kv > 0) ? ext->H_kv : H;
+  a.kw_lo = ext ? ext->kw_lo : nullptr;
+  a.kw_hi = ext ? ext->kw_hi : nullptr;
   a.causal = causal ? 1 : 0;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
   return a;
@@ -187,11 +196,19 @@ cpr_status cp_ring_attn_step(int32_t dtype, int32_t B, int32_t H, int32_t D, con
                              const int32_t* q_pos, const cpr_view* k, const cpr_view* v, int32_t Lk,
                              const int32_t* kv_pos, int32_t causal, float softmax_scale, float* o_acc, float* m,
                              float* l, void* stream) {
-  TRY(validate_attn(dtype, B, H, D, q, Lq, q_pos, k, v, Lk, kv_pos));
+  return cp_ring_attn_step_ex(dtype, B, H, D, q, Lq, q_pos, k, v, Lk, kv_pos, causal, softmax_scale, nullptr,
+                              o_acc, m, l, stream);
+}
+
+cpr_status cp_ring_attn_step_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, const cpr_view* q, int32_t Lq,
+                                const int32_t* q_pos, const cpr_view* k, const cpr_view* v, int32_t Lk,
+                                const int32_t* kv_pos, int32_t causal, float softmax_scale, const cpr_attn_ext* ext,
+                                float* o_acc, float* m, float* l, void* stream) {
+  TRY(validate_attn(dtype, B, H, D, q, Lq, q_pos, k, v, Lk, kv_pos, ext));
   TRY(check_state(0, o_acc, m, l));
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(CPR_EINVAL, "softmax_scale must be finite");
-  AttnArgs a = make_args(dtype, B, H, D, q, Lq, q_pos, k, v, Lk, kv_pos, causal, softmax_scale);
+  AttnArgs a = make_args(dtype, B, H, D, q, Lq, q_pos, k, v, Lk, kv_pos, causal, softmax_scale, ext);
   a.nblocks = 1; a.rank = 0; a.cp = 1;
   a.o_acc = o_acc; a.m = m; a.l = l;
   a.load_state = 1; a.finalize = 0;
@@ -238,9 +255,18 @@ cpr_status cp_ring_attn_run(int32_t dtype, int32_t B, int32_t H, int32_t D, int3
                             const cpr_view* v_ring, const int32_t* ring_pos, int32_t causal, float softmax_scale,
                             void* o_out, float* lse_out, void* workspace, size_t workspace_bytes, int32_t flags,
                             void* stream) {
+  return cp_ring_attn_run_ex(dtype, B, H, D, cp_size, rank, q_local, Lq, q_pos, k_ring, v_ring, ring_pos, causal,
+                             softmax_scale, nullptr, o_out, lse_out, workspace, workspace_bytes, flags, stream);
+}
+
+cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t cp_size, int32_t rank,
+                               const cpr_view* q_local, int32_t Lq, const int32_t* q_pos, const cpr_view* k_ring,
+                               const cpr_view* v_ring, const int32_t* ring_pos, int32_t causal, float softmax_scale,
+                               const cpr_attn_ext* ext, void* o_out, float* lse_out, void* workspace,
+                               size_t workspace_bytes, int32_t flags, void* stream) {
   if (cp_size < 1) return fail(CPR_EINVAL, "cp_size must be >= 1 (got %d)", cp_size);
   if (rank < 0 || rank >= cp_size) return fail(CPR_EINVAL, "rank %d outside [0, %d)", rank, cp_size);
-  TRY(validate_attn(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, (int64_t)Lq * cp_size, ring_pos));
+  TRY(validate_attn(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, (int64_t)Lq * cp_size, ring_pos, ext));
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(CPR_EINVAL, "softmax_scale must be finite");
   if (!o_out) return fail(CPR_EINVAL, "o_out is NULL");
@@ -248,7 +274,8 @@ cpr_status cp_ring_attn_run(int32_t dtype, int32_t B, int32_t H, int32_t D, int3
   if (lse_out && !aligned(lse_out, 4)) return fail(CPR_EINVAL, "lse_out must be 4-byte aligned");
   if (flags != CPR_RUN_FUSED && flags != CPR_RUN_STEPWISE) return fail(CPR_EINVAL, "unknown flags %d", flags);
   const hipStream_t st = static_cast<hipStream_t>(stream);
-  AttnArgs a = make_args(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, Lq, ring_pos, causal, softmax_scale);
+  AttnArgs a = make_args(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, Lq, ring_pos, causal, softmax_scale,
+                         ext);
   if (flags == CPR_RUN_FUSED) {
     a.nblocks = cp_size; a.rank = rank; a.cp = cp_size;
     a.o_out = o_out; a.lse = lse_out;

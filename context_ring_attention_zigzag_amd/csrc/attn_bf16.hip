@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) int32_t pos_lds[4][kBN];
   __shared__ __attribute__((aligned(8))) uint8_t flags8[kMaxTiles];
   __shared__ uint16_t klist[kMaxTiles + kListPad];
-  __shared__ int32_t qrange[2][NW];
+  __shared__ int32_t qrange[4][NW];
   __shared__ int32_t wcount[NW];
 
   const int tid = threadIdx.x;
@@ -224,23 +224,41 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   const int q_idx = q_base + wave * 32 + ql;
   const bool q_in = q_idx < a.Lq;
   const int32_t qp = q_in ? a.q_pos[q_idx] : -1;
+  // key positions this query may attend, [qlow, qlim]: the causal bound and the
+  // optional per-query window; empty (qlim = -1) for a pad query. qlow >= 0,
+  // so pad keys (position -1) always fall outside.
+  int32_t qlow = 0, qlim = -1;
+  if (qp >= 0) {
+    qlow = a.kw_lo ? max(a.kw_lo[q_idx], 0) : 0;
+    qlim = a.causal ? qp : INT_MAX;
+    if (a.kw_hi) qlim = min(qlim, a.kw_hi[q_idx]);
+  }
+  const bool q_live = qlow <= qlim;   // attends some key position
 
-  // ---- valid-position range of the workgroup's queries
-  int qmin, qmax;
+  // ---- bounds over the workgroup's live queries: the lowest and highest
+  // allowed key position any query may attend (lb_min, ub_max) and every query
+  // may attend (lb_max, ub_min)
+  int lb_min, lb_max, ub_min, ub_max;
   {
-    int lo = wave_min(qp >= 0 ? qp : INT_MAX);
-    int hi = wave_max(qp);
+    const int w0 = wave_min(q_live ? qlow : INT_MAX), w1 = wave_max(q_live ? qlow : -1);
+    const int w2 = wave_min(q_live ? qlim : INT_MAX), w3 = wave_max(q_live ? qlim : -1);
     if (lane == 0) {
-      qrange[0][wave] = lo;
-      qrange[1][wave] = hi;
+      qrange[0][wave] = w0;
+      qrange[1][wave] = w1;
+      qrange[2][wave] = w2;
+      qrange[3][wave] = w3;
     }
     __syncthreads();
-    qmin = INT_MAX;
-    qmax = -1;
+    lb_min = INT_MAX;
+    lb_max = -1;
+    ub_min = INT_MAX;
+    ub_max = -1;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      qmin = min(qmin, qrange[0][w]);
-      qmax = max(qmax, qrange[1][w]);
+      lb_min = min(lb_min, qrange[0][w]);
+      lb_max = max(lb_max, qrange[1][w]);
+      ub_min = min(ub_min, qrange[2][w]);
+      ub_max = max(ub_max, qrange[3][w]);
     }
   }
 
@@ -289,10 +307,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;   // finite stand-in while nothing is allowed yet
 
   const float c2 = a.scale * kLog2e;   // score -> log2 units
-  const bool wg_has_queries = qmax >= 0;
+  const bool wg_has_queries = ub_max >= 0;
 
-  const __bf16* kbh = static_cast<const __bf16*>(a.k) + b * a.k_sb + h * a.k_sh;
-  const __bf16* vbh = static_cast<const __bf16*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const int hk = h / (a.H / a.H_kv);   // grouped-query attention: the K/V head of query head h
+  const __bf16* kbh = static_cast<const __bf16*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const __bf16* vbh = static_cast<const __bf16*>(a.v) + b * a.v_sb + hk * a.v_sh;
   const int n_kt = (a.Lk + kBN - 1) / kBN;
 
   // LDS read offsets (elements), loop invariant.
@@ -360,8 +379,10 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
           pad |= __shfl_xor(pad, o);
         }
         if (g16 == 0 && tt < nseg) {
-          const bool keep = kmax >= 0 && (!a.causal || kmin <= qmax);
-          const bool full = !pad && (!a.causal || kmax <= qmin);
+          // kept when the tile's positions meet some query's allowed range; full
+          // when every live query may attend every key of the tile
+          const bool keep = kmax >= 0 && kmax >= lb_min && kmin <= ub_max;
+          const bool full = !pad && kmin >= lb_max && kmax <= ub_min;
           flags8[tt] = (uint8_t)((keep ? 1 : 0) | ((keep && !full) ? 2 : 0));
         }
       }
@@ -536,9 +557,6 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
           // keys of this tile that exist, less this half-wave's key offset: key
           // kt*32 + 8*i + 4*hh + jj exists when kt*32 + 8*i + jj < remh
           const int remh = a.Lk - (seg0 + (e & 0x7fff)) * kBN - 4 * hh;
-          // the causal test pk <= qp becomes pk <= qlim; qlim = INT_MAX when not
-          // causal, -1 for a pad query (which then matches no key: pk >= 0 fails)
-          const int qlim = qp < 0 ? -1 : (a.causal ? qp : INT_MAX);
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -547,7 +565,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
               const int pk[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
               for (int jj = 0; jj < 4; ++jj) {
-                const bool ok = kt * 32 + 8 * i + jj < remh && pk[jj] >= 0 && pk[jj] <= qlim;
+                const bool ok = kt * 32 + 8 * i + jj < remh && pk[jj] >= qlow && pk[jj] <= qlim;
                 s[kt][4 * i + jj] = ok ? s[kt][4 * i + jj] : -INFINITY;
               }
             }
@@ -740,7 +758,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   // ---- epilogue
   const float l_tot = other_half_sum(lsum0 + lsum1);
   if (!q_in) return;
-  const bool has = qp >= 0 && l_tot > 0.f;
+  // a query that may attend no key position (a pad, or an empty window) has no
+  // result even if it took part in an unmasked full tile
+  const bool has = q_live && l_tot > 0.f;
   if (a.finalize) {
     const float inv = has ? 1.0f / l_tot : 0.f;
     __bf16* out = static_cast<__bf16*>(a.o_out) + srow * D;

@@ -40,6 +40,14 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a) {
   const int d0 = sub * DS;
   const bool in_range = row < a.Lq;
   const int32_t qp = in_range ? a.q_pos[row] : -1;
+  // allowed key positions [lb, ub]: causal bound, optional per-query window;
+  // a pad query gets an empty range
+  int32_t lb = 0, ub = -1;
+  if (qp >= 0) {
+    lb = a.kw_lo ? max(a.kw_lo[row], 0) : 0;
+    ub = a.causal ? qp : INT_MAX;
+    if (a.kw_hi) ub = min(ub, a.kw_hi[row]);
+  }
 
   const float* qg = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh;
   float q[DS];
@@ -59,8 +67,9 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a) {
     for (int i = 0; i < DS; ++i) o[i] = 0.f;
   }
 
-  const float* kg = static_cast<const float*>(a.k) + b * a.k_sb + h * a.k_sh;
-  const float* vg = static_cast<const float*>(a.v) + b * a.v_sb + h * a.v_sh;
+  const int hk = h / (a.H / a.H_kv);   // grouped-query attention: the K/V head of query head h
+  const float* kg = static_cast<const float*>(a.k) + b * a.k_sb + hk * a.k_sh;
+  const float* vg = static_cast<const float*>(a.v) + b * a.v_sb + hk * a.v_sh;
 
   for (int t = 0; t < a.nblocks; ++t) {
     int src = (a.rank - t) % a.cp;
@@ -88,7 +97,7 @@ __global__ void __launch_bounds__(256) attn_f32_kernel(AttnArgs a) {
         part += __shfl_xor(part, 1);
         part += __shfl_xor(part, 2);
         const int32_t kp = ps[j];
-        const bool allowed = qp >= 0 && kp >= 0 && (!a.causal || kp <= qp);
+        const bool allowed = kp >= lb && kp <= ub;   // lb >= 0 also excludes pad keys (-1)
         s[j] = allowed ? part * a.scale : -INFINITY;
         tmax = fmaxf(tmax, s[j]);
       }

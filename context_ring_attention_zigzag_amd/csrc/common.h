@@ -30,6 +30,8 @@ struct AttnArgs {
   const void* v; int64_t v_sb, v_sh, v_sl;
   const int32_t* kv_pos;
   int32_t B, H, D, Lq, Lk;
+  int32_t H_kv;                         // K/V heads; query head h reads K/V head h / (H / H_kv)
+  const int32_t* kw_lo; const int32_t* kw_hi;   // per-query key-position window, or NULL
   int32_t nblocks, rank, cp;
   int32_t causal;
   float scale;

@@ -197,6 +197,47 @@ cpr_status cp_ring_attn_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
                             void* o_out, float* lse_out,
                             void* workspace, size_t workspace_bytes, int32_t flags, void* stream);
 
+/*
+ * Extensions of the ring pass for real workloads (all optional: a NULL
+ * extension, or H_kv = 0 and NULL windows, is the plain pass above).
+ *   H_kv   heads of K and V (grouped-query attention): 0 means H; otherwise
+ *          1 <= H_kv and H % H_kv == 0, and query head h reads K/V head
+ *          h / (H / H_kv). The k/v views are then [B, H_kv, L, D]. The
+ *          Megatron page ("Context Parallelism (CP)", communication) counts
+ *          the ring traffic in K/V heads, H_kv.
+ *   kw_lo, kw_hi  int32 device arrays of Lq entries, each may be NULL: query
+ *          i may only attend keys whose position p satisfies
+ *          kw_lo[i] <= p <= kw_hi[i] (in addition to causal masking). This is
+ *          how packed sequences are attended: with the bounds of each query's
+ *          own document, attention never crosses a document boundary. The
+ *          Megatron page ("Implementation quirk: symmetric chunk assignment")
+ *          requires the attention mask and the packed-sequence metadata to
+ *          follow the chunk pairing: the bounds are global positions, given
+ *          per local query in the same order as q_pos.
+ */
+typedef struct cpr_attn_ext {
+  int32_t H_kv;
+  const int32_t* kw_lo;
+  const int32_t* kw_hi;
+} cpr_attn_ext;
+
+/* cp_ring_attn_step with the extensions above; k and v are [B, H_kv, Lk, D]. */
+cpr_status cp_ring_attn_step_ex(int32_t dtype, int32_t B, int32_t H, int32_t D,
+                                const cpr_view* q, int32_t Lq, const int32_t* q_pos,
+                                const cpr_view* k, const cpr_view* v, int32_t Lk, const int32_t* kv_pos,
+                                int32_t causal, float softmax_scale, const cpr_attn_ext* ext,
+                                float* o_acc, float* m, float* l, void* stream);
+
+/* cp_ring_attn_run with the extensions above; k_ring and v_ring are
+ * [B, H_kv, cp_size*Lq, D]. */
+cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D,
+                               int32_t cp_size, int32_t rank,
+                               const cpr_view* q_local, int32_t Lq, const int32_t* q_pos,
+                               const cpr_view* k_ring, const cpr_view* v_ring, const int32_t* ring_pos,
+                               int32_t causal, float softmax_scale, const cpr_attn_ext* ext,
+                               void* o_out, float* lse_out,
+                               void* workspace, size_t workspace_bytes, int32_t flags, void* stream);
+
 /* Static description of a status code. */
 const char* cp_status_string(int32_t status);
 

@@ -33,6 +33,7 @@ from .ring_attention import (  # noqa: F401
     fold_block,
     full_attention,
     init_state,
+    kv_head,
     layout,
     merge,
     padded_len,

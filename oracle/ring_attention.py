@@ -102,7 +102,7 @@ def ring_source(rank: int, t: int, cp: int) -> int:
 # Masking and plain attention.
 # ---------------------------------------------------------------------------
 
-def allowed_mask(q_pos, k_pos, causal: bool):
+def allowed_mask(q_pos, k_pos, causal: bool, kw_lo=None, kw_hi=None):
     """[Nq, Nk] bool: may query i attend key j.
 
     Causal attention keeps the lower-triangular region by global position,
@@ -114,17 +114,25 @@ def allowed_mask(q_pos, k_pos, causal: bool):
     ok = (q_pos >= 0) & (k_pos >= 0)
     if causal:
         ok = ok & (k_pos <= q_pos)
+    # optional per-query window of key positions [kw_lo, kw_hi] (packed
+    # documents: the bounds of the query's own document; the Megatron page,
+    # "Implementation quirk: symmetric chunk assignment", has the attention mask
+    # and packed-sequence metadata follow the chunk pairing, by global position)
+    if kw_lo is not None:
+        ok = ok & (k_pos >= np.asarray(kw_lo)[:, None])
+    if kw_hi is not None:
+        ok = ok & (k_pos <= np.asarray(kw_hi)[:, None])
     return ok
 
 
-def _attend_rows(q, k, v, q_pos, k_pos, causal, scale):
+def _attend_rows(q, k, v, q_pos, k_pos, causal, scale, kw_lo=None, kw_hi=None):
     """Softmax attention for a few query rows of one (b, h).
 
     q [n, D], k/v [Nk, D], float64. Returns O [n, D], LSE [n]. This is the
     textbook definition: s = scale * q k^T, masked softmax over keys, O = P v.
     """
     s = scale * (q @ k.T)
-    ok = allowed_mask(q_pos, k_pos, causal)
+    ok = allowed_mask(q_pos, k_pos, causal, kw_lo, kw_hi)
     s = np.where(ok, s, -np.inf)
     m = s.max(axis=1)
     has = np.isfinite(m)
@@ -138,10 +146,18 @@ def _attend_rows(q, k, v, q_pos, k_pos, causal, scale):
     return o, lse
 
 
-def full_attention(q, k, v, q_pos, k_pos, causal: bool, scale=None, row_chunk: int = 64):
+def kv_head(h: int, n_heads: int, n_kv_heads: int) -> int:
+    """K/V head read by query head h when K/V have fewer heads (grouped-query
+    attention): consecutive groups of H/H_kv query heads share one K/V head."""
+    return h // (n_heads // n_kv_heads)
+
+
+def full_attention(q, k, v, q_pos, k_pos, causal: bool, scale=None, row_chunk: int = 64, kw_lo=None, kw_hi=None):
     """Unpartitioned softmax attention, fp64.
 
-    q [B, H, Nq, D], k/v [B, H, Nk, D]; q_pos [Nq], k_pos [Nk] global positions.
+    q [B, H, Nq, D], k/v [B, H_kv, Nk, D] (H_kv divides H; query head h reads
+    K/V head ``kv_head(h, H, H_kv)``); q_pos [Nq], k_pos [Nk] global positions;
+    kw_lo / kw_hi optional [Nq] key-position windows.
     Returns O [B, H, Nq, D] float64 and LSE [B, H, Nq] float64.
     This is the result ring attention must reproduce up to rounding
     ("Context Parallelism", "How context parallelism works";
@@ -157,22 +173,30 @@ def full_attention(q, k, v, q_pos, k_pos, causal: bool, scale=None, row_chunk: i
     k_pos = np.asarray(k_pos)
     o = np.zeros((b_, h_, nq, v.shape[-1]))
     lse = np.zeros((b_, h_, nq))
+    h_kv = k.shape[1]
+    if h_ % h_kv:
+        raise ValueError("K/V heads must divide query heads")
     for b in range(b_):
         for h in range(h_):
+            hk = kv_head(h, h_, h_kv)
             for r0 in range(0, nq, row_chunk):
                 r1 = min(nq, r0 + row_chunk)
                 o[b, h, r0:r1], lse[b, h, r0:r1] = _attend_rows(
-                    q[b, h, r0:r1], k[b, h], v[b, h], q_pos[r0:r1], k_pos, causal, scale)
+                    q[b, h, r0:r1], k[b, hk], v[b, hk], q_pos[r0:r1], k_pos, causal, scale,
+                    None if kw_lo is None else np.asarray(kw_lo)[r0:r1],
+                    None if kw_hi is None else np.asarray(kw_hi)[r0:r1])
     return o, lse
 
 
 def rank_reference(q, k, v, seq_len: int, cp: int, lay: int, rank: int, causal: bool,
-                   scale=None, rows=None):
+                   scale=None, rows=None, kw_lo_nat=None, kw_hi_nat=None):
     """What rank ``rank`` must output: rows of full attention over the whole sequence.
 
     q, k, v are the unsharded [B, H, seq_len, D] tensors in natural token
     order. The rank's local rows come from ``layout``; ``rows`` optionally
     picks a subset of local row indices (for sampled checks at large sizes).
+    kw_lo_nat / kw_hi_nat optionally give every token's key window in natural
+    order (packed documents); the rank's queries take those of their tokens.
     Returns O [B, H, n, D] and LSE [B, H, n] in local order.
     """
     token_idx, pos_ids = layout(seq_len, cp, lay)
@@ -190,7 +214,15 @@ def rank_reference(q, k, v, seq_len: int, cp: int, lay: int, rank: int, causal: 
     real = local_tok < seq_len
     qsel[:, :, real] = q[:, :, local_tok[real]]
     k_pos = np.arange(seq_len)
-    return full_attention(qsel, k, v, local_pos, k_pos, causal, scale)
+
+    def local_window(nat):
+        if nat is None:
+            return None
+        w = np.zeros(len(local_tok), dtype=np.int64)   # pad queries attend nothing anyway
+        w[real] = np.asarray(nat)[local_tok[real]]
+        return w
+    return full_attention(qsel, k, v, local_pos, k_pos, causal, scale, kw_lo=local_window(kw_lo_nat),
+                          kw_hi=local_window(kw_hi_nat))
 
 
 # ---------------------------------------------------------------------------
@@ -205,7 +237,7 @@ def init_state(b_: int, h_: int, lq: int, d: int):
     return (np.zeros((b_, h_, lq, d)), np.full((b_, h_, lq), -np.inf), np.zeros((b_, h_, lq)))
 
 
-def fold_block(state, q, k_blk, v_blk, q_pos, k_pos, causal: bool, scale=None):
+def fold_block(state, q, k_blk, v_blk, q_pos, k_pos, causal: bool, scale=None, kw_lo=None, kw_hi=None):
     """Fold one arriving KV block into the running (O, m, l).
 
     m is the running max of the allowed scaled scores (natural-log units), l
@@ -219,18 +251,20 @@ def fold_block(state, q, k_blk, v_blk, q_pos, k_pos, causal: bool, scale=None):
     v_blk = np.asarray(v_blk, dtype=np.float64)
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
-    ok = allowed_mask(q_pos, k_pos, causal)
+    ok = allowed_mask(q_pos, k_pos, causal, kw_lo, kw_hi)
     b_, h_ = q.shape[:2]
+    h_kv = k_blk.shape[1]
     for b in range(b_):
         for h in range(h_):
-            s = np.where(ok, scale * (q[b, h] @ k_blk[b, h].T), -np.inf)
+            hk = kv_head(h, h_, h_kv)
+            s = np.where(ok, scale * (q[b, h] @ k_blk[b, hk].T), -np.inf)
             m_new = np.maximum(m[b, h], s.max(axis=1))
             fin = np.isfinite(m_new)
             m_use = np.where(fin, m_new, 0.0)
             alpha = np.where(np.isfinite(m[b, h]), np.exp(m[b, h] - m_use), 0.0)
             p = np.where(ok, np.exp(s - m_use[:, None]), 0.0)
             l[b, h] = alpha * l[b, h] + p.sum(axis=1)
-            o[b, h] = alpha[:, None] * o[b, h] + p @ v_blk[b, h]
+            o[b, h] = alpha[:, None] * o[b, h] + p @ v_blk[b, hk]
             m[b, h] = m_new
     return o, m, l
 
@@ -262,7 +296,7 @@ def finalize(state):
 
 
 def ring_emulation(q_local, k_ring, v_ring, q_pos, ring_pos, cp: int, rank: int, causal: bool,
-                   scale=None, order=None, keep_states: bool = False):
+                   scale=None, order=None, keep_states: bool = False, kw_lo=None, kw_hi=None):
     """One rank's whole ring pass, block by block, in fp64.
 
     q_local [B, H, Lq, D] with global positions q_pos [Lq]; k_ring/v_ring
@@ -284,7 +318,7 @@ def ring_emulation(q_local, k_ring, v_ring, q_pos, ring_pos, cp: int, rank: int,
         src = ring_source(rank, t, cp) if order is None else t
         sl = slice(src * lk, (src + 1) * lk)
         state = fold_block(state, q_local, np.asarray(k_ring)[:, :, sl], np.asarray(v_ring)[:, :, sl],
-                           q_pos, np.asarray(ring_pos)[sl], causal, scale)
+                           q_pos, np.asarray(ring_pos)[sl], causal, scale, kw_lo, kw_hi)
         if keep_states:
             states.append(state)
     out = finalize(state)

@@ -106,3 +106,21 @@ def sample_rows(n_local: int, chunk: int, count: int, seed: int) -> np.ndarray:
     if extra:
         picks.update(int(x) for x in rng.integers(0, n_local, size=extra))
     return np.array(sorted(picks), dtype=np.int64)
+
+
+def packed_windows(doc_lens, causal: bool):
+    """Key-position windows of a packed sequence, in natural token order.
+
+    Documents of the given lengths are packed back to back; token t of the
+    document [a, a + n) may attend keys at positions [a, a + n - 1] (the causal
+    bound, when asked for, is applied by the attention itself). Returns int32
+    (lo, hi) arrays of sum(doc_lens) entries. Input metadata only: both the
+    HIP path and the oracle consume it.
+    """
+    lo, hi = [], []
+    a = 0
+    for n in doc_lens:
+        lo += [a] * n
+        hi += [a + n - 1] * n
+        a += n
+    return np.asarray(lo, dtype=np.int32), np.asarray(hi, dtype=np.int32)

@@ -189,3 +189,20 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(cpr, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         cpr.load(str(tmp_path / "nope.so"))
+
+
+def test_extension_validation(lib):
+    """cp_ring_attn_run_ex rejects K/V head counts that do not divide H, before touching any memory."""
+    q, k, v = view(), view(), view()
+    p = fake_ptr()
+    for h_kv in (3, -1, 5):
+        ext = cpr.CprAttnExt(h_kv, None, None)
+        st = lib.cp_ring_attn_run_ex(cpr.BF16, 1, 4, 128, 2, 0, ctypes.byref(q), 128, p, ctypes.byref(k),
+                                     ctypes.byref(v), p, 1, 0.0, ctypes.byref(ext), p, None, None, 0,
+                                     cpr.RUN_FUSED, None)
+        assert st == cpr.EINVAL
+    ext = cpr.CprAttnExt(2, ctypes.c_void_p(0x100002), None)   # misaligned window array
+    st = lib.cp_ring_attn_run_ex(cpr.BF16, 1, 4, 128, 2, 0, ctypes.byref(q), 128, p, ctypes.byref(k), ctypes.byref(v),
+                                 p, 1, 0.0, ctypes.byref(ext), p, None, None, 0, cpr.RUN_FUSED, None)
+    assert st == cpr.EINVAL
+

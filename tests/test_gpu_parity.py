@@ -18,7 +18,7 @@ import torch
 import oracle
 import context_ring_attention_zigzag_amd as cpr
 from context_ring_attention_zigzag_amd import device_inputs as di
-from seeded_inputs import WORKLOADS, gen_slice, sample_rows, small_workload
+from seeded_inputs import WORKLOADS, gen_slice, packed_windows, sample_rows, small_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -171,6 +171,92 @@ def test_ragged_and_padded(case):
             o, lse, _ = run_rank(w, dev, r, flags)
             ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], S, cp, lay, r, causal)
             compare(o, lse, ro, rl, dtype, f"{case} r{r} f{flags}")
+
+
+# ------------------------------- grouped-query attention and key windows
+
+def run_rank_ext(w, q_nat, k_nat, v_nat, rank, flags, lo_nat=None, hi_nat=None):
+    """run_rank with K/V of their own head count and optional natural-order key windows."""
+    ri = di.prepare_rank(q_nat, k_nat, v_nat, w.S, w.cp, lay_code(w), rank)
+    o = torch.empty_like(ri.q_local)
+    lse = torch.empty(ri.q_local.shape[:3], dtype=torch.float32, device="cuda")
+    ws = None
+    if flags == cpr.RUN_STEPWISE:
+        ws = torch.empty(cpr.cp_ring_attn_workspace_size(w.B, w.H, ri.lq, w.D), dtype=torch.uint8, device="cuda")
+    kw = [None, None]
+    tok = ri.token_idx[rank * ri.lq:(rank + 1) * ri.lq].long()
+    real = tok < w.S
+    for i, nat in enumerate((lo_nat, hi_nat)):
+        if nat is not None:
+            nat_d = torch.from_numpy(np.asarray(nat, dtype=np.int32)).cuda()
+            kw[i] = torch.where(real, nat_d[tok.clamp(max=w.S - 1)], 0).to(torch.int32).contiguous()
+    cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, w.causal, 0.0, o, lse,
+                         ws, flags, kw_lo=kw[0], kw_hi=kw[1])
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+GQA = [
+    # dtype, D, S, cp, layout, causal, H, H_kv
+    ("bf16", 128, 1000, 4, "zigzag", True, 8, 2),
+    ("bf16", 64, 513, 2, "contiguous", False, 4, 1),
+    ("f32", 64, 201, 3, "striped", True, 6, 3),
+    ("bf16", 128, 700, 3, "striped", True, 4, 2),
+]
+
+
+@pytest.mark.parametrize("case", GQA, ids=lambda c: "-".join(map(str, c)))
+def test_grouped_query_attention(case):
+    dtype, D, S, cp, layout, causal, H, H_kv = case
+    w = small_workload("gqa", dtype, 1, H, D, S, cp, layout, causal, seed=zlib.crc32(repr(case).encode()) % 1000)
+    dev, host = natural_inputs(w)
+    k_nat, v_nat = dev["k"][:, :H_kv].contiguous(), dev["v"][:, :H_kv].contiguous()
+    hk, hv = host["k"][:, :H_kv], host["v"][:, :H_kv]
+    for r in range(cp):
+        ro, rl = oracle.rank_reference(host["q"], hk, hv, S, cp, ORACLE_LAYS[layout], r, causal)
+        for flags in (cpr.RUN_FUSED, cpr.RUN_STEPWISE):
+            o, lse = run_rank_ext(w, dev["q"], k_nat, v_nat, r, flags)
+            compare(o, lse, ro, rl, dtype, f"{case} r{r} f{flags}")
+
+
+DOCS = [
+    # dtype, D, S, cp, layout, causal, document lengths
+    ("bf16", 128, 1000, 4, "zigzag", True, (300, 1, 64, 200, 435)),
+    ("bf16", 64, 777, 3, "striped", True, (100, 677)),
+    ("bf16", 128, 513, 2, "contiguous", False, (13, 500)),
+    ("f32", 64, 201, 3, "zigzag", True, (50, 50, 101)),
+]
+
+
+@pytest.mark.parametrize("case", DOCS, ids=lambda c: "-".join(map(str, c[:6])) + f"-{len(c[6])}docs")
+def test_packed_documents(case):
+    dtype, D, S, cp, layout, causal, docs = case
+    assert sum(docs) == S
+    w = small_workload("docs", dtype, 1, 2, D, S, cp, layout, causal, seed=zlib.crc32(repr(case).encode()) % 1000)
+    dev, host = natural_inputs(w)
+    lo, hi = packed_windows(docs, causal)
+    for r in range(cp):
+        ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], S, cp, ORACLE_LAYS[layout], r, causal,
+                                       kw_lo_nat=lo, kw_hi_nat=hi)
+        for flags in (cpr.RUN_FUSED, cpr.RUN_STEPWISE):
+            o, lse = run_rank_ext(w, dev["q"], dev["k"], dev["v"], r, flags, lo, hi)
+            compare(o, lse, ro, rl, dtype, f"{case[:6]} r{r} f{flags}")
+
+
+def test_sliding_window_with_empty_windows():
+    """Causal window of 100 keys; every 7th query gets an empty window (hi < lo): O = 0, LSE = -inf there."""
+    w = small_workload("window", "bf16", 1, 2, 128, 1500, 4, "zigzag", True, seed=21)
+    dev, host = natural_inputs(w)
+    t = np.arange(w.S)
+    lo = np.maximum(t - 100, 0).astype(np.int32)
+    hi = np.where(t % 7 == 3, lo - 1, t).astype(np.int32)
+    for r in range(w.cp):
+        ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], w.S, w.cp, oracle.ZIGZAG, r, True,
+                                       kw_lo_nat=lo, kw_hi_nat=hi)
+        assert np.isneginf(rl).any()
+        for flags in (cpr.RUN_FUSED, cpr.RUN_STEPWISE):
+            o, lse = run_rank_ext(w, dev["q"], dev["k"], dev["v"], r, flags, lo, hi)
+            compare(o, lse, ro, rl, "bf16", f"window r{r} f{flags}")
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])

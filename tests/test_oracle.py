@@ -18,7 +18,7 @@ import torch
 
 import oracle
 from oracle import ring_attention as ora
-from seeded_inputs import WORKLOADS, gen_tensor, small_workload
+from seeded_inputs import WORKLOADS, gen_tensor, packed_windows, small_workload
 
 ZZ, CT, ST = oracle.ZIGZAG, oracle.CONTIGUOUS, oracle.STRIPED
 LAYOUTS = {"zigzag": ZZ, "contiguous": CT, "striped": ST}
@@ -355,10 +355,114 @@ def test_workload_pair_counts():
             assert total == oracle.causal_pairs_zigzag(w.S, w.cp)
 
 
+# ------------------------------------- grouped-query attention, key windows
+
+def brute_force_windows(q, k, v, qpos, kpos, causal, scale, lo, hi):
+    """Scalar pure-Python attention where query i may attend keys with lo[i] <= pos <= hi[i]."""
+    outs, lses = [], []
+    for i in range(len(q)):
+        keys = [j for j in range(len(k)) if qpos[i] >= 0 and kpos[j] >= 0 and (not causal or kpos[j] <= qpos[i])
+                and lo[i] <= kpos[j] <= hi[i]]
+        if not keys:
+            outs.append([0.0] * len(v[0]))
+            lses.append(-math.inf)
+            continue
+        s = {j: scale * sum(a * b for a, b in zip(q[i], k[j])) for j in keys}
+        mx = max(s.values())
+        w = {j: math.exp(s[j] - mx) for j in keys}
+        z = sum(w.values())
+        outs.append([sum(w[j] * v[j][t] for j in keys) / z for t in range(len(v[0]))])
+        lses.append(mx + math.log(z))
+    return np.array(outs), np.array(lses)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_windows_vs_brute_force(causal, seed):
+    rng = np.random.default_rng(100 + seed)
+    nq, nk, d = 11, 14, 3
+    q, k, v = rnd((1, 1, nq, d), seed + 50), rnd((1, 1, nk, d), seed + 60), rnd((1, 1, nk, d), seed + 70)
+    qpos = rng.permutation(nk)[:nq]
+    qpos[2] = -1                                   # a pad query
+    kpos = np.arange(nk)
+    kpos[5] = -1                                   # a pad key
+    lo = rng.integers(0, nk, nq)
+    hi = lo + rng.integers(-2, 8, nq)              # some windows empty (hi < lo)
+    o, lse = oracle.full_attention(q, k, v, qpos, kpos, causal, kw_lo=lo, kw_hi=hi)
+    ob, lb = brute_force_windows(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), qpos, kpos, causal,
+                                 1 / math.sqrt(d), lo, hi)
+    np.testing.assert_allclose(o[0, 0], ob, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isneginf(lse[0, 0]), np.isneginf(lb))
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(lse[0, 0][fin], lb[fin], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_documents_equal_separate_attention(causal):
+    """Windows bounded by each token's document == attention run on each document alone."""
+    docs = [5, 9, 1, 16, 3]
+    s, d = sum(docs), 4
+    q, k, v = rnd((1, 2, s, d), 80), rnd((1, 2, s, d), 81), rnd((1, 2, s, d), 82)
+    lo, hi = packed_windows(docs, causal)
+    pos = np.arange(s)
+    o, lse = oracle.full_attention(q, k, v, pos, pos, causal, kw_lo=lo, kw_hi=hi)
+    a = 0
+    for n in docs:
+        sl = slice(a, a + n)
+        loc = np.arange(n)   # each document on its own, positions from 0
+        od, ld = oracle.full_attention(q[:, :, sl], k[:, :, sl], v[:, :, sl], loc, loc, causal)
+        np.testing.assert_allclose(o[:, :, sl], od, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[:, :, sl], ld, rtol=0, atol=1e-12)
+        a += n
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("h_kv", [1, 2, 4])
+def test_grouped_query_attention_vs_torch_sdpa(causal, h_kv):
+    h, s, d = 4, 17, 8
+    q, k, v = rnd((2, h, s, d), 90), rnd((2, h_kv, s, d), 91), rnd((2, h_kv, s, d), 92)
+    pos = np.arange(s)
+    o, _ = oracle.full_attention(q, k, v, pos, pos, causal)
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
+                                                           torch.from_numpy(v), is_causal=causal, enable_gqa=True)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    assert [oracle.kv_head(x, h, h_kv) for x in range(h)] == [x // (h // h_kv) for x in range(h)]
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous", "striped"])
+def test_ring_emulation_with_gqa_and_documents(layout):
+    """The blockwise ring pass with K/V head groups and document windows == plain attention over the rank's rows."""
+    cp, docs, h, h_kv, d = 4, [7, 20, 3, 1, 19], 4, 2, 6
+    s = sum(docs)
+    lay = LAYOUTS[layout]
+    q, k, v = rnd((1, h, s, d), 93), rnd((1, h_kv, s, d), 94), rnd((1, h_kv, s, d), 95)
+    lo_nat, hi_nat = packed_windows(docs, True)
+    tok, pos = oracle.layout(s, cp, lay)
+    s_pad, lr = len(tok), len(tok) // cp
+    real = tok < s
+
+    def gather(x):
+        out = np.zeros(x.shape[:2] + (s_pad, x.shape[-1]))
+        out[:, :, real] = x[:, :, tok[real]]
+        return out
+    qr, kr, vr = gather(q), gather(k), gather(v)
+    for r in range(cp):
+        sl = slice(r * lr, (r + 1) * lr)
+        ltok = tok[sl]
+        lo = np.where(ltok < s, lo_nat[np.minimum(ltok, s - 1)], 0)
+        hi = np.where(ltok < s, hi_nat[np.minimum(ltok, s - 1)], 0)
+        o, lse = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, cp, r, True, kw_lo=lo, kw_hi=hi)
+        ro, rl = oracle.rank_reference(q, k, v, s, cp, lay, r, True, kw_lo_nat=lo_nat, kw_hi_nat=hi_nat)
+        np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+        np.testing.assert_array_equal(np.isneginf(lse), np.isneginf(rl))
+        fin = np.isfinite(rl)
+        np.testing.assert_allclose(lse[fin], rl[fin], rtol=0, atol=1e-12)
+
+
 # ------------------------------------------------- planted mistakes must fail
 
 def test_planted_strict_mask_is_caught(monkeypatch):
-    def strict(q_pos, k_pos, causal):
+    def strict(q_pos, k_pos, causal, kw_lo=None, kw_hi=None):
         q_pos = np.asarray(q_pos)[:, None]
         k_pos = np.asarray(k_pos)[None, :]
         ok = (q_pos >= 0) & (k_pos >= 0)
@@ -400,7 +504,7 @@ def test_planted_wrong_chunk_pairing_is_caught(monkeypatch, golden_dir):
 def test_planted_wrong_rescale_sign_is_caught(monkeypatch):
     """A fold that rescales earlier partial sums by exp(m_new - m) instead of
     exp(m - m_new) must break the ring == full-attention pin."""
-    def bad_fold(state, q, k_blk, v_blk, q_pos, k_pos, causal, scale=None):
+    def bad_fold(state, q, k_blk, v_blk, q_pos, k_pos, causal, scale=None, kw_lo=None, kw_hi=None):
         o, m, l = (np.array(x, dtype=np.float64) for x in state)
         scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
         ok = ora.allowed_mask(q_pos, k_pos, causal)
@@ -432,7 +536,7 @@ def test_planted_swapped_operands_are_caught(monkeypatch):
     """Attention that multiplies P by K instead of V must fail the torch SDPA pin."""
     orig = ora._attend_rows
 
-    def swapped(q, k, v, q_pos, k_pos, causal, scale):
+    def swapped(q, k, v, q_pos, k_pos, causal, scale, kw_lo=None, kw_hi=None):
         return orig(q, k, k, q_pos, k_pos, causal, scale)
     monkeypatch.setattr(ora, "_attend_rows", swapped)
     s, d = 16, 8
