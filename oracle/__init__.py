@@ -26,6 +26,7 @@ from .ring_attention import (  # noqa: F401
     STRIPED,
     ZIGZAG,
     allowed_mask,
+    attention_backward,
     causal_pairs_striped,
     causal_pairs_zigzag,
     count_pairs,
@@ -38,6 +39,7 @@ from .ring_attention import (  # noqa: F401
     merge,
     padded_len,
     rank_reference,
+    ring_backward,
     ring_emulation,
     ring_source,
 )

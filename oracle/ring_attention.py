@@ -19,7 +19,12 @@ Readings where the pages are silent (each also listed in the design notes):
   query (or any query with no allowed key) yields O = 0 and LSE = -inf;
 * LSE is in natural-log units;
 * ring step t of rank r folds the block that started on rank (r - t) mod cp
-  (blocks move to the next device each hop).
+  (blocks move to the next device each hop);
+* the backward pass (the glossary page's example calls .backward() on the
+  context-parallel output) is the textbook softmax-attention derivative; in
+  the ring each rank recomputes a block's probabilities from the LSE its
+  forward pass saved, keeps its dQ, and adds its dK, dV contributions to the
+  block, which carries them around the ring back to the block's owner.
 """
 
 from __future__ import annotations
@@ -323,6 +328,99 @@ def ring_emulation(q_local, k_ring, v_ring, q_pos, ring_pos, cp: int, rank: int,
             states.append(state)
     out = finalize(state)
     return (out, states) if keep_states else out
+
+
+# ---------------------------------------------------------------------------
+# Backward pass. The glossary page's example ("Context Parallelism",
+# "Practical use and trade-offs") calls .backward() on the context-parallel
+# attention output: the gradients of softmax attention, here the textbook
+# derivative written out, and the same gradients taken block by block in ring
+# order with the log-sum-exp saved by the forward pass.
+# ---------------------------------------------------------------------------
+
+def _score_grad(p, dp, dvec):
+    """dL/dS for S -> P = softmax(S): P * (dP - rowsum(dO * O)), the softmax Jacobian applied row by row."""
+    return p * (dp - dvec[:, None])
+
+
+def attention_backward(q, k, v, do, q_pos, k_pos, causal: bool, scale=None, kw_lo=None, kw_hi=None):
+    """Gradients of O = softmax(scale * Q K^T + mask) V with respect to Q, K, V, fp64.
+
+    q, do [B, H, Nq, D]; k, v [B, H_kv, Nk, D] (query head h reads K/V head
+    kv_head(h, H, H_kv), so dK and dV sum over the heads of a group). With
+    P the masked softmax, O = P V and Dvec = rowsum(dO * O):
+    dV = P^T dO, dP = dO V^T, dS = P * (dP - Dvec), dQ = scale * dS K,
+    dK = scale * dS^T Q. Rows that may attend no key have P = 0 and dQ = 0.
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    b_, h_, nq, d = q.shape
+    h_kv = k.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    ok = allowed_mask(q_pos, k_pos, causal, kw_lo, kw_hi)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(b_):
+        for h in range(h_):
+            hk = kv_head(h, h_, h_kv)
+            s = np.where(ok, scale * (q[b, h] @ k[b, hk].T), -np.inf)
+            m = s.max(axis=1)
+            has = np.isfinite(m)
+            p = np.where(ok, np.exp(s - np.where(has, m, 0.0)[:, None]), 0.0)
+            l = p.sum(axis=1)
+            p[has] /= l[has, None]
+            o = p @ v[b, hk]
+            dvec = (do[b, h] * o).sum(axis=1)
+            dv[b, hk] += p.T @ do[b, h]
+            dp = do[b, h] @ v[b, hk].T
+            ds = _score_grad(p, dp, dvec)
+            dq[b, h] = scale * (ds @ k[b, hk])
+            dk[b, hk] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv
+
+
+def ring_backward(q_local, k_ring, v_ring, o_local, do_local, lse_local, q_pos, ring_pos, cp: int, rank: int,
+                  causal: bool, scale=None, kw_lo=None, kw_hi=None):
+    """One rank's backward ring pass, block by block, fp64.
+
+    Inputs as for ``ring_emulation`` plus the rank's forward output O, the
+    upstream gradient dO and the saved LSE [B, H, Lq]. Each step recomputes the
+    block's probabilities P = exp(scale * q k^T - LSE) (the saved LSE makes
+    them final, no rescaling), accumulates the rank's dQ locally and adds the
+    rank's contributions to the block's dK and dV, which travel with the block
+    around the ring. Returns dQ [B, H, Lq, D] and the contributions
+    dK, dV [B, H_kv, S_pad, D] in ring order.
+    """
+    q, o, do, lse = (np.asarray(x, dtype=np.float64) for x in (q_local, o_local, do_local, lse_local))
+    k_ring = np.asarray(k_ring, dtype=np.float64)
+    v_ring = np.asarray(v_ring, dtype=np.float64)
+    b_, h_, lq, d = q.shape
+    h_kv = k_ring.shape[1]
+    s_pad = k_ring.shape[2]
+    lk = s_pad // cp
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dvec = (do * o).sum(axis=-1)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k_ring)
+    dv = np.zeros_like(v_ring)
+    for t in range(cp):
+        src = ring_source(rank, t, cp)
+        sl = slice(src * lk, (src + 1) * lk)
+        ok = allowed_mask(q_pos, np.asarray(ring_pos)[sl], causal, kw_lo, kw_hi)
+        for b in range(b_):
+            for h in range(h_):
+                hk = kv_head(h, h_, h_kv)
+                s = scale * (q[b, h] @ k_ring[b, hk, sl].T)
+                fin = np.isfinite(lse[b, h])
+                p = np.where(ok & fin[:, None], np.exp(s - np.where(fin, lse[b, h], 0.0)[:, None]), 0.0)
+                dv[b, hk, sl] += p.T @ do[b, h]
+                dp = do[b, h] @ v_ring[b, hk, sl].T
+                ds = _score_grad(p, dp, dvec[b, h])
+                dq[b, h] += scale * (ds @ k_ring[b, hk, sl])
+                dk[b, hk, sl] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv
 
 
 # ---------------------------------------------------------------------------

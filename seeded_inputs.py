@@ -18,7 +18,7 @@ import dataclasses
 import numpy as np
 import torch
 
-TENSOR_IDS = {"q": 0, "k": 1, "v": 2}
+TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "do": 3}   # "do": the upstream gradient dL/dO of the backward pass
 
 
 @dataclasses.dataclass(frozen=True)

@@ -546,3 +546,169 @@ def test_planted_swapped_operands_are_caught(monkeypatch):
     ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k),
                                                            torch.from_numpy(v), is_causal=True).numpy()
     assert np.abs(o - ref).max() > 1e-3
+
+
+# ------------------------------------------------------------- backward pins
+
+def torch_grads(q, k, v, do, mask, scale):
+    """dQ, dK, dV from torch autograd (float64) through torch's own SDPA with a boolean mask."""
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask), scale=scale,
+                                                         enable_gqa=k.shape[1] != q.shape[1])
+    o.backward(torch.from_numpy(do))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("h_kv", [1, 2, 4])
+def test_backward_vs_torch_autograd(causal, h_kv):
+    h, nq, nk, d = 4, 13, 21, 8
+    q, do = rnd((2, h, nq, d), 100), rnd((2, h, nq, d), 101)
+    k, v = rnd((2, h_kv, nk, d), 102), rnd((2, h_kv, nk, d), 103)
+    qpos, kpos = np.arange(8, 8 + nq), np.arange(nk)
+    scale = 0.3
+    got = oracle.attention_backward(q, k, v, do, qpos, kpos, causal, scale)
+    want = torch_grads(q, k, v, do, oracle.allowed_mask(qpos, kpos, causal), scale)
+    for g, w_ in zip(got, want):
+        np.testing.assert_allclose(g, w_, rtol=0, atol=1e-12)
+
+
+def test_backward_with_windows_vs_torch_autograd():
+    docs, h, d = [5, 11, 2, 9], 2, 6
+    s = sum(docs)
+    lo, hi = packed_windows(docs, True)
+    hi = np.minimum(hi, np.arange(s))
+    lo = np.maximum(lo, np.arange(s) - 4)             # plus a sliding window of 5 keys
+    q, k, v, do = (rnd((1, h, s, d), 104 + i) for i in range(4))
+    pos = np.arange(s)
+    got = oracle.attention_backward(q, k, v, do, pos, pos, True, kw_lo=lo, kw_hi=hi)
+    want = torch_grads(q, k, v, do, oracle.allowed_mask(pos, pos, True, lo, hi), 1 / math.sqrt(d))
+    for g, w_ in zip(got, want):
+        np.testing.assert_allclose(g, w_, rtol=0, atol=1e-12)
+
+
+def test_backward_vs_finite_differences():
+    """Central differences of L = sum(dO * O) in fp64, independent of any autograd."""
+    h, h_kv, nq, nk, d = 2, 1, 5, 7, 4
+    q, do = rnd((1, h, nq, d), 110), rnd((1, h, nq, d), 111)
+    k, v = rnd((1, h_kv, nk, d), 112), rnd((1, h_kv, nk, d), 113)
+    qpos, kpos = np.arange(2, 2 + nq), np.arange(nk)
+
+    def loss(q_, k_, v_):
+        o, _ = oracle.full_attention(q_, k_, v_, qpos, kpos, True)
+        return float((do * o).sum())
+    grads = oracle.attention_backward(q, k, v, do, qpos, kpos, True)
+    eps = 1e-6
+    for which, g in enumerate(grads):
+        xs = [q.copy(), k.copy(), v.copy()]
+        for idx in np.ndindex(xs[which].shape):
+            xp = [x.copy() for x in xs]
+            xm = [x.copy() for x in xs]
+            xp[which][idx] += eps
+            xm[which][idx] -= eps
+            num = (loss(*xp) - loss(*xm)) / (2 * eps)
+            assert abs(num - g[idx]) < 1e-7, (which, idx, num, g[idx])
+
+
+def test_backward_empty_rows_and_zero_upstream():
+    """Rows with no allowed key get dQ = 0 and add nothing to dK, dV; dO = 0 gives all-zero gradients."""
+    q, do = rnd((1, 1, 4, 3), 120), rnd((1, 1, 4, 3), 121)
+    k, v = rnd((1, 1, 6, 3), 122), rnd((1, 1, 6, 3), 123)
+    qpos, kpos = np.array([0, 1, -1, 3]), np.arange(2, 8)        # rows 0, 1 see no key (causal), row 2 is a pad
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, qpos, kpos, True)
+    assert (dq[0, 0, :3] == 0).all()
+    keep = np.array([False, False, False, True])
+    dq2, dk2, dv2 = oracle.attention_backward(q[:, :, keep], k, v, do[:, :, keep], qpos[keep], kpos, True)
+    np.testing.assert_allclose(dk, dk2, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(dv, dv2, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(dq[:, :, keep], dq2, rtol=0, atol=1e-15)
+    z = oracle.attention_backward(q, k, v, np.zeros_like(do), qpos, kpos, True)
+    assert all((g == 0).all() for g in z)
+
+
+def test_backward_closed_form_single_key():
+    """One allowed key per row: P = 1, so dV = sum of dO over the rows, dQ = dK = 0."""
+    q, do = rnd((1, 1, 3, 4), 124), rnd((1, 1, 3, 4), 125)
+    k, v = rnd((1, 1, 5, 4), 126), rnd((1, 1, 5, 4), 127)
+    lo = hi = np.array([2, 2, 2])
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, np.arange(3), np.arange(5), False, kw_lo=lo, kw_hi=hi)
+    assert np.abs(dq).max() < 1e-15 and np.abs(dk).max() < 1e-15
+    np.testing.assert_allclose(dv[0, 0, 2], do[0, 0].sum(axis=0), rtol=0, atol=1e-15)
+    assert (np.delete(dv[0, 0], 2, axis=0) == 0).all()
+
+
+def ring_backward_all_ranks(q, k, v, do, s, cp, lay, causal, lo_nat=None, hi_nat=None):
+    """Run the forward and backward ring pass on every rank; return dQ in natural order and the
+    dK, dV contributions summed over ranks, also in natural order."""
+    tok, pos = oracle.layout(s, cp, lay)
+    s_pad, lr = len(tok), len(tok) // cp
+    real = tok < s
+
+    def gather(x):
+        out = np.zeros(x.shape[:2] + (s_pad, x.shape[-1]))
+        out[:, :, real] = x[:, :, tok[real]]
+        return out
+    qr, kr, vr, dor = gather(q), gather(k), gather(v), gather(do)
+    dq_r = np.zeros_like(qr)
+    dk_r, dv_r = np.zeros_like(kr), np.zeros_like(vr)
+    for r in range(cp):
+        sl = slice(r * lr, (r + 1) * lr)
+        ltok = tok[sl]
+        lo = hi = None
+        if lo_nat is not None:
+            lo = np.where(ltok < s, lo_nat[np.minimum(ltok, s - 1)], 0)
+            hi = np.where(ltok < s, hi_nat[np.minimum(ltok, s - 1)], 0)
+        o, lse = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, cp, r, causal, kw_lo=lo, kw_hi=hi)
+        dq, dk, dv = oracle.ring_backward(qr[:, :, sl], kr, vr, o, dor[:, :, sl], lse, pos[sl], pos, cp, r, causal,
+                                          kw_lo=lo, kw_hi=hi)
+        dq_r[:, :, sl] = dq
+        dk_r += dk
+        dv_r += dv
+    inv = np.empty(s_pad, np.int64)
+    inv[tok] = np.arange(s_pad)
+    nat = inv[:s]
+    return dq_r[:, :, nat], dk_r[:, :, nat], dv_r[:, :, nat], (dq_r[:, :, ~real], dk_r[:, :, ~real], dv_r[:, :, ~real])
+
+
+@pytest.mark.parametrize("cp", [1, 2, 4, 8])
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous", "striped"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ring_backward_equals_full_gradients(cp, layout, causal):
+    """Per-rank dQ and the dK, dV contributions summed over the ring == gradients of plain attention."""
+    w = small_workload("t", "f32", 1, 2, 8, 53, cp, layout, causal, seed=cp * 10 + causal + 1)
+    q, k, v = (gen_tensor(w, t).astype(np.float64) for t in "qkv")
+    do = gen_tensor(w, "do").astype(np.float64)
+    dq, dk, dv, pads = ring_backward_all_ranks(q, k, v, do, w.S, cp, LAYOUTS[layout], causal)
+    nat = np.arange(w.S)
+    want = oracle.attention_backward(q, k, v, do, nat, nat, causal)
+    for g, w_ in zip((dq, dk, dv), want):
+        np.testing.assert_allclose(g, w_, rtol=0, atol=1e-12)
+    assert all((p == 0).all() for p in pads)                       # pad rows get and give nothing
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "striped"])
+def test_ring_backward_with_gqa_and_documents(layout):
+    cp, docs, h, h_kv, d = 4, [7, 20, 3, 1, 19], 4, 2, 6
+    s = sum(docs)
+    q, do = rnd((1, h, s, d), 130), rnd((1, h, s, d), 131)
+    k, v = rnd((1, h_kv, s, d), 132), rnd((1, h_kv, s, d), 133)
+    lo, hi = packed_windows(docs, True)
+    dq, dk, dv, _ = ring_backward_all_ranks(q, k, v, do, s, cp, LAYOUTS[layout], True, lo, hi)
+    nat = np.arange(s)
+    want = oracle.attention_backward(q, k, v, do, nat, nat, True, kw_lo=lo, kw_hi=hi)
+    for g, w_ in zip((dq, dk, dv), want):
+        np.testing.assert_allclose(g, w_, rtol=0, atol=1e-12)
+
+
+def test_planted_backward_without_dvec_is_caught(monkeypatch):
+    """dS = P * dP (the row term rowsum(dO * O) dropped) must fail the autograd pin."""
+    monkeypatch.setattr(ora, "_score_grad", lambda p, dp, dvec: p * dp)
+    with pytest.raises(AssertionError):
+        test_backward_vs_torch_autograd(False, 4)
+
+
+def test_planted_wrong_kv_head_group_is_caught(monkeypatch):
+    """Query head h reading K/V head h mod H_kv (instead of h // (H / H_kv)) must fail the autograd pin."""
+    monkeypatch.setattr(ora, "kv_head", lambda h, n_h, n_kv: h % n_kv)
+    with pytest.raises(AssertionError):
+        test_backward_vs_torch_autograd(True, 2)
