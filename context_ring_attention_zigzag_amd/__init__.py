@@ -30,7 +30,8 @@ OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 EXPORTS = (
     "cp_padded_len", "cp_zigzag_partition", "cp_shard_gather", "cp_ring_attn_init", "cp_ring_attn_step",
     "cp_ring_attn_merge", "cp_ring_attn_finalize", "cp_ring_attn_workspace_size", "cp_ring_attn_run",
-    "cp_ring_attn_step_ex", "cp_ring_attn_run_ex", "cp_status_string", "cp_last_error",
+    "cp_ring_attn_step_ex", "cp_ring_attn_run_ex", "cp_ring_attn_bwd_workspace_size", "cp_ring_attn_bwd_prep",
+    "cp_ring_attn_bwd_step", "cp_ring_attn_bwd_run", "cp_status_string", "cp_last_error",
 )
 
 
@@ -79,6 +80,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        vp]),
         "cp_ring_attn_run_ex": (i32, [i32, i32, i32, i32, i32, i32, pv, i32, vp, pv, pv, vp, i32, f32, pe, vp, vp,
                                       vp, ctypes.c_size_t, i32, vp]),
+        "cp_ring_attn_bwd_workspace_size": (ctypes.c_size_t, [i32, i32, i32]),
+        "cp_ring_attn_bwd_prep": (i32, [i32, i32, i32, i32, i32, pv, pv, vp, vp, i32, pe, vp, ctypes.c_size_t, vp]),
+        "cp_ring_attn_bwd_step": (i32, [i32, i32, i32, i32, i32, pv, pv, i32, pv, pv, i32, vp, f32, vp,
+                                        ctypes.c_size_t, vp, vp, vp, vp]),
+        "cp_ring_attn_bwd_run": (i32, [i32, i32, i32, i32, i32, i32, pv, i32, vp, pv, pv, vp, pv, pv, vp, i32, f32,
+                                       pe, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "cp_status_string": (ctypes.c_char_p, [i32]),
         "cp_last_error": (ctypes.c_char_p, []),
     }
@@ -201,3 +208,59 @@ def cp_ring_attn_run(q_local, q_pos, k_ring, v_ring, ring_pos, cp_size: int, ran
                                       int(bool(causal)), float(softmax_scale), ctypes.byref(ext), _ptr(o_out),
                                       _ptr(lse_out), _ptr(workspace), ws_bytes, flags, _stream(stream)),
            "cp_ring_attn_run_ex")
+
+
+# ------------------------------------------------------------ backward pass
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def _win_ext(h_kv: int, kw_lo, kw_hi):
+    if h_kv == 0 and kw_lo is None and kw_hi is None:
+        return None
+    return CprAttnExt(h_kv, None if kw_lo is None else kw_lo.data_ptr(), None if kw_hi is None else kw_hi.data_ptr())
+
+
+def cp_ring_attn_bwd_workspace_size(B: int, H: int, Lq: int) -> int:
+    return load().cp_ring_attn_bwd_workspace_size(B, H, Lq)
+
+
+def cp_ring_attn_bwd_prep(o, do, lse, q_pos, causal: bool, workspace, kw_lo=None, kw_hi=None, stream=None):
+    """Per-row {LSE * log2(e), rowsum(dO * O)} and per-query key windows into `workspace`."""
+    B, H, Lq, D = o.shape
+    ov, gv = view(o), view(do)
+    ext = _win_ext(0, kw_lo, kw_hi)
+    _check(load().cp_ring_attn_bwd_prep(dtype_code(o), B, H, D, Lq, ctypes.byref(ov), ctypes.byref(gv), _ptr(lse),
+                                        _ptr(q_pos), int(bool(causal)), None if ext is None else ctypes.byref(ext),
+                                        _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "cp_ring_attn_bwd_prep")
+
+
+def cp_ring_attn_bwd_step(q, do, k, v, kv_pos, softmax_scale: float, workspace, dq_acc, dk_acc, dv_acc,
+                          stream=None):
+    """Add one KV block's contributions: dq_acc [B,H,Lq,D], dk_acc and dv_acc [B,H_kv,Lk,D] (float32)."""
+    B, H, Lq, D = q.shape
+    qv, gv, kv, vv = view(q), view(do), view(k), view(v)
+    _check(load().cp_ring_attn_bwd_step(dtype_code(q), B, H, D, k.shape[1], ctypes.byref(qv), ctypes.byref(gv), Lq,
+                                        ctypes.byref(kv), ctypes.byref(vv), k.shape[2], _ptr(kv_pos),
+                                        float(softmax_scale), _ptr(workspace), _nbytes(workspace), _ptr(dq_acc),
+                                        _ptr(dk_acc), _ptr(dv_acc), _stream(stream)),
+           "cp_ring_attn_bwd_step")
+
+
+def cp_ring_attn_bwd_run(q_local, q_pos, k_ring, v_ring, ring_pos, cp_size: int, rank: int, o_local, do_local,
+                         lse_local, causal: bool, softmax_scale: float, dq, dk, dv, workspace, stream=None,
+                         kw_lo=None, kw_hi=None):
+    """One rank's backward ring pass: writes dq [B,H,Lq,D] and the rank's share of every block's
+    dk, dv [B,H_kv,cp*Lq,D] (float32), in ring order."""
+    B, H, Lq, D = q_local.shape
+    qv, kv, vv, ov, gv = view(q_local), view(k_ring), view(v_ring), view(o_local), view(do_local)
+    h_kv = k_ring.shape[1]
+    ext = _win_ext(0 if h_kv == H else h_kv, kw_lo, kw_hi)
+    _check(load().cp_ring_attn_bwd_run(dtype_code(q_local), B, H, D, cp_size, rank, ctypes.byref(qv), Lq,
+                                       _ptr(q_pos), ctypes.byref(kv), ctypes.byref(vv), _ptr(ring_pos),
+                                       ctypes.byref(ov), ctypes.byref(gv), _ptr(lse_local), int(bool(causal)),
+                                       float(softmax_scale), None if ext is None else ctypes.byref(ext), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "cp_ring_attn_bwd_run")

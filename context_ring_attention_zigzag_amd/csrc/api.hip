@@ -47,6 +47,7 @@ cpr_status check_view(const char* name, const cpr_view* v, int32_t dtype) {
   if (!v->data) return fail(CPR_EINVAL, "%s: data pointer is NULL", name);
   if (v->stride_b < 0 || v->stride_h < 0 || v->stride_l < 0)
     return fail(CPR_EINVAL, "%s: negative stride", name);
+  if (v->stride_l > ((int64_t)1 << 24)) return fail(CPR_EUNSUPPORTED, "%s: stride_l must be <= 2^24", name);
   const int64_t align_elems = dtype == CPR_BF16 ? 8 : 1;   // 16-byte rows for bf16
   if (dtype == CPR_BF16) {
     if (!aligned(v->data, 16)) return fail(CPR_EINVAL, "%s: bf16 data must be 16-byte aligned", name);
@@ -166,6 +167,7 @@ static cpr_status validate_attn(int32_t dtype, int32_t B, int32_t H, int32_t D, 
   TRY(check_view("v", v, dtype));
   if (!q_pos || !kv_pos) return fail(CPR_EINVAL, "position arrays must be non-NULL");
   TRY(check_grid(B, H, Lq));
+  TRY(check_grid(B, ext && ext->H_kv > 0 ? ext->H_kv : H, (int32_t)Lk_total));   // Lk_total <= 2^30 here
   return CPR_OK;
 }
 
@@ -302,6 +304,143 @@ cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, i
   }
   return hip_status(launch_finalize(dtype == CPR_BF16, (int64_t)rows, D, o_acc, m, l, o_out, lse_out, st),
                     "cp_ring_attn_run(finalize)");
+}
+
+// ------------------------------------------------------------- backward
+
+size_t cp_ring_attn_bwd_workspace_size(int32_t B, int32_t H, int32_t Lq) {
+  if (B < 1 || H < 1 || Lq < 1 || Lq > CPR_MAX_SEQ) return 0;
+  return round256((size_t)B * H * Lq * 8) + round256((size_t)Lq * 8);
+}
+
+static cpr_status check_bwd_workspace(int32_t B, int32_t H, int32_t Lq, const void* ws, size_t bytes) {
+  const size_t need = cp_ring_attn_bwd_workspace_size(B, H, Lq);
+  if (!ws || bytes < need) return fail(CPR_EINVAL, "backward workspace needs %zu bytes", need);
+  if (!aligned(ws, 256)) return fail(CPR_EINVAL, "backward workspace must be 256-byte aligned");
+  return CPR_OK;
+}
+
+static void bwd_workspace(void* ws, int32_t B, int32_t H, int32_t Lq, float2** qinfo, int2** qwin) {
+  char* w = static_cast<char*>(ws);
+  *qinfo = reinterpret_cast<float2*>(w);
+  *qwin = reinterpret_cast<int2*>(w + round256((size_t)B * H * Lq * 8));
+}
+
+static cpr_status check_grad(const char* name, const float* p) {
+  if (!p) return fail(CPR_EINVAL, "%s is NULL", name);
+  if (!aligned(p, 16)) return fail(CPR_EINVAL, "%s must be 16-byte aligned", name);
+  return CPR_OK;
+}
+
+// float32 views read 16 bytes at a time by the preprocessing pass
+static cpr_status check_rows16(const char* name, const cpr_view* v, int32_t dtype) {
+  if (dtype == CPR_F32 && (!aligned(v->data, 16) || v->stride_b % 4 || v->stride_h % 4 || v->stride_l % 4))
+    return fail(CPR_EINVAL, "%s: float32 rows must be 16-byte aligned", name);
+  return CPR_OK;
+}
+
+cpr_status cp_ring_attn_bwd_prep(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t Lq,
+                                 const cpr_view* o_local, const cpr_view* do_local, const float* lse_local,
+                                 const int32_t* q_pos, int32_t causal, const cpr_attn_ext* ext,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  TRY(check_dims(dtype, B, H, D));
+  TRY(check_len("Lq", Lq));
+  TRY(check_view("o_local", o_local, dtype));
+  TRY(check_view("do_local", do_local, dtype));
+  TRY(check_rows16("o_local", o_local, dtype));
+  TRY(check_rows16("do_local", do_local, dtype));
+  if (!lse_local || !aligned(lse_local, 4)) return fail(CPR_EINVAL, "lse_local must be non-NULL and 4-byte aligned");
+  if (!q_pos) return fail(CPR_EINVAL, "q_pos is NULL");
+  if (ext && ((ext->kw_lo && !aligned(ext->kw_lo, 4)) || (ext->kw_hi && !aligned(ext->kw_hi, 4))))
+    return fail(CPR_EINVAL, "key-window arrays must be 4-byte aligned");
+  TRY(check_bwd_workspace(B, H, Lq, workspace, workspace_bytes));
+  BwdPrepArgs a{};
+  a.o = o_local->data; a.o_sb = o_local->stride_b; a.o_sh = o_local->stride_h; a.o_sl = o_local->stride_l;
+  a.dout = do_local->data; a.do_sb = do_local->stride_b; a.do_sh = do_local->stride_h; a.do_sl = do_local->stride_l;
+  a.lse = lse_local;
+  a.q_pos = q_pos;
+  a.kw_lo = ext ? ext->kw_lo : nullptr;
+  a.kw_hi = ext ? ext->kw_hi : nullptr;
+  a.causal = causal ? 1 : 0;
+  a.B = B; a.H = H; a.D = D; a.Lq = Lq;
+  bwd_workspace(workspace, B, H, Lq, &a.qinfo, &a.qwin);
+  return hip_status(launch_bwd_prep(dtype == CPR_BF16, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_bwd_prep");
+}
+
+static BwdArgs make_bwd_args(int32_t B, int32_t H, int32_t D, int32_t H_kv, const cpr_view* q,
+                             const cpr_view* dout, int32_t Lq, const cpr_view* k, const cpr_view* v, int32_t Lk,
+                             const int32_t* kv_pos, float softmax_scale, void* workspace) {
+  BwdArgs a{};
+  a.q = q->data; a.q_sb = q->stride_b; a.q_sh = q->stride_h; a.q_sl = q->stride_l;
+  a.dout = dout->data; a.do_sb = dout->stride_b; a.do_sh = dout->stride_h; a.do_sl = dout->stride_l;
+  a.k = k->data; a.k_sb = k->stride_b; a.k_sh = k->stride_h; a.k_sl = k->stride_l;
+  a.v = v->data; a.v_sb = v->stride_b; a.v_sh = v->stride_h; a.v_sl = v->stride_l;
+  a.kv_pos = kv_pos;
+  float2* qinfo;
+  int2* qwin;
+  bwd_workspace(workspace, B, H, Lq, &qinfo, &qwin);
+  a.qinfo = qinfo;
+  a.qwin = qwin;
+  a.B = B; a.H = H; a.H_kv = H_kv > 0 ? H_kv : H; a.D = D; a.Lq = Lq; a.Lk = Lk;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);
+  return a;
+}
+
+static hipError_t launch_bwd(int32_t dtype, const BwdArgs& a, hipStream_t st) {
+  return dtype == CPR_BF16 ? launch_bwd_bf16(a, 1, 1, st) : launch_bwd_f32(a, 1, 1, st);
+}
+
+cpr_status cp_ring_attn_bwd_step(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t H_kv,
+                                 const cpr_view* q, const cpr_view* dout, int32_t Lq,
+                                 const cpr_view* k, const cpr_view* v, int32_t Lk, const int32_t* kv_pos,
+                                 float softmax_scale, const void* workspace, size_t workspace_bytes,
+                                 float* dq_acc, float* dk_acc, float* dv_acc, void* stream) {
+  // the step takes no query positions (the windows come with the workspace):
+  // kv_pos stands in for the non-NULL check of q_pos
+  cpr_attn_ext ext{H_kv, nullptr, nullptr};
+  TRY(validate_attn(dtype, B, H, D, q, Lq, kv_pos, k, v, Lk, kv_pos, &ext));
+  TRY(check_view("dout", dout, dtype));
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
+    return fail(CPR_EINVAL, "softmax_scale must be finite");
+  TRY(check_bwd_workspace(B, H, Lq, workspace, workspace_bytes));
+  TRY(check_grad("dq_acc", dq_acc));
+  TRY(check_grad("dk_acc", dk_acc));
+  TRY(check_grad("dv_acc", dv_acc));
+  BwdArgs a = make_bwd_args(B, H, D, H_kv, q, dout, Lq, k, v, Lk, kv_pos, softmax_scale,
+                            const_cast<void*>(workspace));
+  a.nblocks = 1; a.rank = 0; a.cp = 1;
+  a.dq = dq_acc; a.dk = dk_acc; a.dv = dv_acc;
+  a.accumulate = 1;
+  return hip_status(launch_bwd(dtype, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_bwd_step");
+}
+
+cpr_status cp_ring_attn_bwd_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
+                                int32_t cp_size, int32_t rank,
+                                const cpr_view* q_local, int32_t Lq, const int32_t* q_pos,
+                                const cpr_view* k_ring, const cpr_view* v_ring, const int32_t* ring_pos,
+                                const cpr_view* o_local, const cpr_view* do_local, const float* lse_local,
+                                int32_t causal, float softmax_scale, const cpr_attn_ext* ext,
+                                float* dq_local, float* dk_ring, float* dv_ring,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (cp_size < 1) return fail(CPR_EINVAL, "cp_size must be >= 1 (got %d)", cp_size);
+  if (rank < 0 || rank >= cp_size) return fail(CPR_EINVAL, "rank %d outside [0, %d)", rank, cp_size);
+  TRY(validate_attn(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, (int64_t)Lq * cp_size, ring_pos, ext));
+  if ((int64_t)Lq * cp_size > CPR_MAX_SEQ) return fail(CPR_EUNSUPPORTED, "cp_size * Lq must be <= 2^30");
+  if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
+    return fail(CPR_EINVAL, "softmax_scale must be finite");
+  TRY(check_grad("dq_local", dq_local));
+  TRY(check_grad("dk_ring", dk_ring));
+  TRY(check_grad("dv_ring", dv_ring));
+  // the preprocessing validates o_local, do_local, lse_local and the workspace
+  TRY(cp_ring_attn_bwd_prep(dtype, B, H, D, Lq, o_local, do_local, lse_local, q_pos, causal, ext, workspace,
+                            workspace_bytes, stream));
+  const int32_t h_kv = ext ? ext->H_kv : 0;
+  BwdArgs a = make_bwd_args(B, H, D, h_kv, q_local, do_local, Lq, k_ring, v_ring, Lq, ring_pos, softmax_scale,
+                            workspace);
+  a.nblocks = cp_size; a.rank = rank; a.cp = cp_size;
+  a.dq = dq_local; a.dk = dk_ring; a.dv = dv_ring;
+  a.accumulate = 0;
+  return hip_status(launch_bwd(dtype, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_bwd_run");
 }
 
 const char* cp_status_string(int32_t status) {

@@ -40,6 +40,44 @@ struct AttnArgs {
   int32_t load_state, finalize;
 };
 
+// Backward pass. Preprocessing, per query row: qinfo = {LSE in log2 units (+inf
+// for a row that attends no key), rowsum(dO * O)}; per query: qwin = {lo, hi},
+// the key positions it may attend (empty when lo > hi).
+struct BwdPrepArgs {
+  const void* o; int64_t o_sb, o_sh, o_sl;
+  const void* dout; int64_t do_sb, do_sh, do_sl;
+  const float* lse;                     // [B, H, Lq], natural log
+  const int32_t* q_pos; const int32_t* kw_lo; const int32_t* kw_hi;
+  int32_t causal;
+  int32_t B, H, D, Lq;
+  float2* qinfo;                        // [B, H, Lq]
+  int2* qwin;                           // [Lq]
+};
+
+// Gradient kernels. The dQ kernel folds `nblocks` KV blocks of Lk rows in
+// ring order (block t is block (rank - t) mod cp of k/v/kv_pos); the dK/dV
+// kernel covers all nblocks * Lk rows of k/v at once. Outputs are fp32,
+// contiguous: dq [B, H, Lq, D], dk and dv [B, H_kv, nblocks * Lk, D]; with
+// accumulate set they are added to, else written.
+struct BwdArgs {
+  const void* q; int64_t q_sb, q_sh, q_sl;
+  const void* dout; int64_t do_sb, do_sh, do_sl;
+  const void* k; int64_t k_sb, k_sh, k_sl;
+  const void* v; int64_t v_sb, v_sh, v_sl;
+  const int32_t* kv_pos;
+  const float2* qinfo;
+  const int2* qwin;
+  int32_t B, H, H_kv, D, Lq, Lk;
+  int32_t nblocks, rank, cp;
+  float scale;
+  float* dq; float* dk; float* dv;
+  int32_t accumulate;
+};
+
+hipError_t launch_bwd_prep(int32_t dtype_bf16, const BwdPrepArgs& a, hipStream_t st);
+hipError_t launch_bwd_bf16(const BwdArgs& a, int32_t do_dq, int32_t do_dkv, hipStream_t st);
+hipError_t launch_bwd_f32(const BwdArgs& a, int32_t do_dq, int32_t do_dkv, hipStream_t st);
+
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
 

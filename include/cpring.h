@@ -1,6 +1,6 @@
 /*
  * cpring.h - C ABI of libcpring: one context-parallel rank's ring-attention
- * forward pass, for AMD Instinct MI355X (gfx950).
+ * forward and backward passes, for AMD Instinct MI355X (gfx950).
  *
  * Method (pages cited by title and section):
  *  - "Context Parallelism" (Ultralytics glossary), "How context parallelism
@@ -237,6 +237,84 @@ cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D,
                                int32_t causal, float softmax_scale, const cpr_attn_ext* ext,
                                void* o_out, float* lse_out,
                                void* workspace, size_t workspace_bytes, int32_t flags, void* stream);
+
+/*
+ * Backward pass: the gradients of one rank's attention output (the glossary
+ * page, "Context Parallelism", "Practical use and trade-offs", differentiates
+ * the context-parallel output). With O and LSE saved by the forward pass and
+ * dO the gradient of the loss with respect to O, for every block the rank sees:
+ *   P    = exp(scale * q k^T - LSE), the final probabilities, recomputed
+ *          (masked entries 0; a query with LSE = -inf has P = 0);
+ *   Dvec = rowsum(dO * O), dP = dO v^T, dS = P * (dP - Dvec);
+ *   dQ   = scale * dS k, summed over every block: it stays on the rank;
+ *   dK   = scale * dS^T q and dV = P^T dO: this rank's share of the block's
+ *          gradient. In a ring these travel with their block and reach its
+ *          owner after a full circle, summed over the ranks ("Sequence
+ *          Parallelism and Ring Attention", "Deep dive": blocks move to the
+ *          next device each hop).
+ * dtype CPR_BF16 runs on bf16 MFMA with float32 accumulation: P and dS are
+ * rounded to bf16 (nearest even) before the products that use them. CPR_F32
+ * runs in float32. Gradients are float32, contiguous. The masking rules, the
+ * extensions (cpr_attn_ext) and the softmax_scale default are the forward's.
+ */
+
+/* Workspace bytes of the backward pass for B*H*Lq query rows: a float2
+ * {LSE * log2(e), Dvec} per row, then an int2 {lo, hi} allowed key-position
+ * window per query. Returns 0 for invalid sizes. */
+size_t cp_ring_attn_bwd_workspace_size(int32_t B, int32_t H, int32_t Lq);
+
+/*
+ * Backward preprocessing of one rank's queries, once per backward pass. Fills
+ * `workspace` (cp_ring_attn_bwd_workspace_size(B, H, Lq) bytes, 256-byte
+ * aligned) from:
+ *   o_local, do_local  [B,H,Lq,D] views of dtype: the forward output and dO
+ *                      (float32 views need 16-byte aligned rows);
+ *   lse_local          [B,H,Lq] contiguous float32: the forward's LSE;
+ *   q_pos, causal, ext the forward's positions, causal flag and windows
+ *                      (only the windows of ext are used here).
+ */
+cpr_status cp_ring_attn_bwd_prep(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t Lq,
+                                 const cpr_view* o_local, const cpr_view* do_local, const float* lse_local,
+                                 const int32_t* q_pos, int32_t causal, const cpr_attn_ext* ext,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One backward ring step: add the contributions of one KV block.
+ *   q, dout    [B,H,Lq,D] views of dtype: local queries and dO;
+ *   k, v       [B,H_kv,Lk,D] views of dtype: the block (H_kv = 0 means H),
+ *              positions kv_pos [Lk];
+ *   workspace  filled by cp_ring_attn_bwd_prep for these queries;
+ *   dq_acc     [B,H,Lq,D] float32: dq_acc += scale * dS k;
+ *   dk_acc, dv_acc  [B,H_kv,Lk,D] float32: += the rank's share of the
+ *              block's dK and dV (the buffers that travel with the block).
+ * The accumulators must not overlap the inputs or each other.
+ */
+cpr_status cp_ring_attn_bwd_step(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t H_kv,
+                                 const cpr_view* q, const cpr_view* dout, int32_t Lq,
+                                 const cpr_view* k, const cpr_view* v, int32_t Lk, const int32_t* kv_pos,
+                                 float softmax_scale, const void* workspace, size_t workspace_bytes,
+                                 float* dq_acc, float* dk_acc, float* dv_acc, void* stream);
+
+/*
+ * One rank's whole backward ring pass, the counterpart of cp_ring_attn_run_ex
+ * (q_local, q_pos, k_ring, v_ring, ring_pos, causal, softmax_scale and ext as
+ * there): preprocessing, dQ over every block in ring order, and the rank's
+ * share of dK and dV of every block.
+ *   o_local, do_local  [B,H,Lq,D] views of dtype; lse_local [B,H,Lq] float32;
+ *   dq_local   [B,H,Lq,D] float32, written;
+ *   dk_ring, dv_ring  [B,H_kv,cp_size*Lq,D] float32, written, in ring order
+ *              like k_ring: summed over all ranks they are the full
+ *              gradients of K and V;
+ *   workspace  cp_ring_attn_bwd_workspace_size(B, H, Lq) bytes, 256-byte aligned.
+ */
+cpr_status cp_ring_attn_bwd_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
+                                int32_t cp_size, int32_t rank,
+                                const cpr_view* q_local, int32_t Lq, const int32_t* q_pos,
+                                const cpr_view* k_ring, const cpr_view* v_ring, const int32_t* ring_pos,
+                                const cpr_view* o_local, const cpr_view* do_local, const float* lse_local,
+                                int32_t causal, float softmax_scale, const cpr_attn_ext* ext,
+                                float* dq_local, float* dk_ring, float* dv_ring,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* cp_status_string(int32_t status);

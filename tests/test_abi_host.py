@@ -206,3 +206,44 @@ def test_extension_validation(lib):
                                  p, 1, 0.0, ctypes.byref(ext), p, None, None, 0, cpr.RUN_FUSED, None)
     assert st == cpr.EINVAL
 
+
+
+def test_bwd_workspace_size(lib):
+    ws = lib.cp_ring_attn_bwd_workspace_size(2, 16, 8192)
+    assert ws >= 2 * 16 * 8192 * 8 + 8192 * 8 and ws % 256 == 0
+    assert lib.cp_ring_attn_bwd_workspace_size(0, 1, 8) == 0
+    assert lib.cp_ring_attn_bwd_workspace_size(1, 1, 0) == 0
+
+
+def test_bwd_validation(lib):
+    """The backward entry points reject bad arguments before launching anything."""
+    p = fake_ptr()
+    q, k, v, o, g = view(), view(), view(), view(), view()
+    need = lib.cp_ring_attn_bwd_workspace_size(1, 2, 64)
+
+    def prep(dtype=cpr.BF16, D=128, lse=p, ws=p, nbytes=need, ov=o):
+        return lib.cp_ring_attn_bwd_prep(dtype, 1, 2, D, 64, ctypes.byref(ov), ctypes.byref(g), lse, p, 1, None, ws,
+                                         nbytes, None)
+    assert prep(lse=None) == cpr.EINVAL and "lse" in err(lib)
+    assert prep(ws=None) == cpr.EINVAL and "workspace" in err(lib)
+    assert prep(nbytes=need - 1) == cpr.EINVAL
+    assert prep(ws=fake_ptr(0x100010)) == cpr.EINVAL and "256-byte" in err(lib)
+    assert prep(D=96) == cpr.EUNSUPPORTED
+    assert prep(dtype=cpr.F32, ov=view(sl=130)) == cpr.EINVAL and "16-byte" in err(lib)
+
+    def step(h_kv=0, dq=p, ws=p, nbytes=need, scale=0.0):
+        return lib.cp_ring_attn_bwd_step(cpr.BF16, 1, 2, 128, h_kv, ctypes.byref(q), ctypes.byref(g), 64,
+                                         ctypes.byref(k), ctypes.byref(v), 64, p, scale, ws, nbytes, dq, p, p, None)
+    assert step(h_kv=3) == cpr.EINVAL and "H_kv" in err(lib)
+    assert step(dq=None) == cpr.EINVAL and "dq_acc" in err(lib)
+    assert step(dq=fake_ptr(0x100004)) == cpr.EINVAL and "16-byte" in err(lib)
+    assert step(nbytes=0) == cpr.EINVAL and "workspace" in err(lib)
+    assert step(scale=float("nan")) == cpr.EINVAL
+
+    def run(cp=2, rank=0, dk=p):
+        return lib.cp_ring_attn_bwd_run(cpr.BF16, 1, 2, 128, cp, rank, ctypes.byref(q), 64, p, ctypes.byref(k),
+                                        ctypes.byref(v), p, ctypes.byref(o), ctypes.byref(g), p, 1, 0.0, None, p, dk,
+                                        p, p, need, None)
+    assert run(cp=0) == cpr.EINVAL
+    assert run(rank=2) == cpr.EINVAL and "rank" in err(lib)
+    assert run(dk=None) == cpr.EINVAL and "dk_ring" in err(lib)

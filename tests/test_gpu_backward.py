@@ -1,0 +1,204 @@
+"""GPU parity of the backward ring pass (C ABI) against the fp64 oracle.
+
+Inputs: seeded Q, K, V and the upstream gradient dO, rounded to the kernel
+dtype; O and LSE come from the oracle's forward ring pass (O rounded to the
+kernel dtype, LSE to float32) and the oracle's backward takes those same
+rounded values, so both sides differentiate the same thing.
+
+Bars (normwise, per gradient tensor): max|g - g_ref| <= tol * max|g_ref|,
+tol = 1e-2 for bf16 and 1e-5 for float32. The bf16 kernels round the
+probabilities P and the score gradients dS to bf16 (relative error up to
+2^-9 each) before the products that use them; a numpy emulation of exactly
+those two roundings gives normwise errors of 1.3e-3 .. 2.8e-3 on the shapes
+below, so 1e-2 keeps a margin of about 3.5x. Zero rows (pads, queries with
+an empty window, keys nobody may attend) must come out exactly zero.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import context_ring_attention_zigzag_amd as cpr
+from context_ring_attention_zigzag_amd import device_inputs as di
+from seeded_inputs import packed_windows
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "f32": 1e-5}
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+LAY = {"zigzag": (cpr.ZIGZAG, oracle.ZIGZAG), "contiguous": (cpr.CONTIGUOUS, oracle.CONTIGUOUS),
+       "striped": (cpr.STRIPED, oracle.STRIPED)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    cpr.load()
+    yield
+
+
+def note(msg):
+    print(f"[gpu-backward] {msg}", flush=True)
+
+
+def rounded(x, dtype):
+    """(device tensor of dtype, float64 host copy of the same values)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(TDT[dtype])
+    return t.cuda(), t.float().numpy().astype(np.float64)
+
+
+def check(got, ref, dtype, what, zero_rows=None):
+    """Normwise bar; rows in zero_rows (a mask over dim 2: rows with nothing allowed) must be exactly 0."""
+    ref_max = float(np.abs(ref).max())
+    err = float(np.abs(got - ref).max())
+    note(f"{what}: max|err|={err:.3e} max|ref|={ref_max:.3e} ratio={err / max(ref_max, 1e-30):.3e}")
+    assert np.isfinite(got).all(), what
+    assert err <= TOL[dtype] * ref_max + 1e-30, f"{what}: {err} > {TOL[dtype]} * {ref_max}"
+    if zero_rows is not None:
+        assert np.all(got[:, :, zero_rows] == 0), f"{what}: rows with nothing allowed are not zero"
+
+
+class Case:
+    """Seeded natural-order inputs of one backward parity case, on host and device."""
+
+    def __init__(self, dtype, B, H, H_kv, D, S, cp, layout, causal, seed, docs=None, scale=1.0):
+        rng = np.random.default_rng(seed)
+        self.dtype, self.B, self.H, self.H_kv, self.D, self.S, self.cp = dtype, B, H, H_kv, D, S, cp
+        self.causal = causal
+        self.lay_c, self.lay_o = LAY[layout]
+        self.dev, self.host = {}, {}
+        for t, heads, sc in (("q", H, scale), ("k", H_kv, scale), ("v", H_kv, 1.0), ("do", H, 1.0)):
+            self.dev[t], self.host[t] = rounded(rng.standard_normal((B, heads, S, D)) * sc, dtype)
+        self.tok, self.pos = oracle.layout(S, cp, self.lay_o)
+        self.s_pad = len(self.tok)
+        self.lq = self.s_pad // cp
+        self.lo_nat = self.hi_nat = None
+        if docs is not None:
+            self.lo_nat, self.hi_nat = packed_windows(docs, causal)
+
+    def host_gather(self, x, idx):
+        out = np.zeros(x.shape[:2] + (len(idx), x.shape[-1]))
+        real = idx < self.S
+        out[:, :, real] = x[:, :, idx[real]]
+        return out
+
+    def rank(self, r):
+        """Everything rank r needs, on both sides."""
+        sl = slice(r * self.lq, (r + 1) * self.lq)
+        ltok = self.tok[sl]
+        ri = di.prepare_rank(self.dev["q"], self.dev["k"], self.dev["v"], self.S, self.cp, self.lay_c, r)
+        do_local = di.gather(self.dev["do"], self.S, ri.token_idx[sl])
+        h = {t: self.host_gather(self.host[t], self.tok) for t in ("k", "v")}
+        h["q"] = self.host_gather(self.host["q"], ltok)
+        h["do"] = self.host_gather(self.host["do"], ltok)
+        lo = hi = None
+        kw = {}
+        if self.lo_nat is not None:
+            lo = np.where(ltok < self.S, self.lo_nat[np.minimum(ltok, self.S - 1)], 0)
+            hi = np.where(ltok < self.S, self.hi_nat[np.minimum(ltok, self.S - 1)], 0)
+            kw = dict(kw_lo=torch.from_numpy(lo.astype(np.int32)).cuda(),
+                      kw_hi=torch.from_numpy(hi.astype(np.int32)).cuda())
+        o, lse = oracle.ring_emulation(h["q"], h["k"], h["v"], self.pos[sl], self.pos, self.cp, r, self.causal,
+                                       kw_lo=lo, kw_hi=hi)
+        o_dev, o_in = rounded(o, self.dtype)
+        lse_dev = torch.from_numpy(lse.astype(np.float32)).cuda()
+        lse_in = lse.astype(np.float32).astype(np.float64)
+        ref = oracle.ring_backward(h["q"], h["k"], h["v"], o_in, h["do"], lse_in, self.pos[sl], self.pos, self.cp,
+                                   r, self.causal, kw_lo=lo, kw_hi=hi)
+        ok = oracle.allowed_mask(self.pos[sl], self.pos, self.causal, lo, hi)
+        self.zero_rows = (~ok.any(axis=1), ~ok.any(axis=0), ~ok.any(axis=0))   # dQ, dK, dV
+        return ri, do_local, o_dev, lse_dev, kw, ref
+
+    def run_gpu(self, r, ri, do_local, o_dev, lse_dev, kw):
+        dq = torch.full(ri.q_local.shape, float("nan"), dtype=torch.float32, device="cuda")
+        dk = torch.full(ri.k_ring.shape, float("nan"), dtype=torch.float32, device="cuda")
+        dv = torch.full(ri.v_ring.shape, float("nan"), dtype=torch.float32, device="cuda")
+        ws = torch.empty(cpr.cp_ring_attn_bwd_workspace_size(self.B, self.H, self.lq), dtype=torch.uint8,
+                         device="cuda")
+        cpr.cp_ring_attn_bwd_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, self.cp, r, o_dev,
+                                 do_local, lse_dev, self.causal, 0.0, dq, dk, dv, ws, **kw)
+        torch.cuda.synchronize()
+        return dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
+
+
+def run_case(c: Case, ranks, name):
+    for r in ranks:
+        note(f"{name} rank {r}: B={c.B} H={c.H} H_kv={c.H_kv} D={c.D} S={c.S} cp={c.cp} causal={c.causal}")
+        ri, do_local, o_dev, lse_dev, kw, ref = c.rank(r)
+        got = c.run_gpu(r, ri, do_local, o_dev, lse_dev, kw)
+        for g, rf, z, n in zip(got, ref, c.zero_rows, ("dQ", "dK", "dV")):
+            check(g, rf, c.dtype, f"{name} r{r} {n}", z)
+
+
+def test_bwd_f32_tiny():
+    c = Case("f32", 1, 2, 2, 64, 256, 2, "zigzag", True, seed=301)
+    run_case(c, (0, 1), "f32_tiny")
+
+
+def test_bwd_bf16_example_shape():
+    c = Case("bf16", 1, 4, 4, 64, 4096, 2, "zigzag", True, seed=302)
+    run_case(c, (0, 1), "bf16_4k")
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "contiguous", "striped"])
+def test_bwd_bf16_ragged_d128(layout):
+    """A sequence that does not fill the tiles (pads in the ring, partial tiles) on every rank."""
+    c = Case("bf16", 2, 2, 2, 128, 1000, 4, layout, True, seed=303)
+    run_case(c, range(4), f"bf16_ragged_{layout}")
+
+
+def test_bwd_bf16_noncausal():
+    c = Case("bf16", 1, 3, 3, 128, 777, 3, "contiguous", False, seed=304)
+    run_case(c, (0, 2), "bf16_noncausal")
+
+
+@pytest.mark.parametrize("dtype,h,h_kv,d", [("bf16", 8, 2, 128), ("bf16", 4, 1, 64), ("f32", 6, 3, 64)])
+def test_bwd_gqa(dtype, h, h_kv, d):
+    c = Case(dtype, 1, h, h_kv, d, 1536 if dtype == "bf16" else 384, 2, "zigzag", True, seed=305)
+    run_case(c, (0, 1), f"{dtype}_gqa_{h}_{h_kv}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_packed_documents(dtype):
+    """Per-query document windows (packed sequences) with grouped-query heads and striped layout."""
+    docs = [300, 5, 700, 1, 250, 44] if dtype == "bf16" else [100, 5, 77, 1, 50]
+    c = Case(dtype, 1, 4, 2, 128 if dtype == "bf16" else 64, sum(docs), 4, "striped", True, seed=306, docs=docs)
+    run_case(c, (0, 3), f"{dtype}_docs")
+
+
+def test_bwd_large_scores():
+    """Scores spread over a wide range (scaled Q and K): the saved LSE makes P exact at any scale."""
+    c = Case("bf16", 1, 2, 2, 128, 2048, 2, "zigzag", True, seed=307, scale=3.0)
+    run_case(c, (0, 1), "bf16_large_scores")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_step_equals_run(dtype):
+    """Prep + one step per ring block, accumulating into per-block dK/dV buffers as a real ring would,
+    gives the result of the whole-pass call (summation order aside)."""
+    c = Case(dtype, 1, 4, 2, 128 if dtype == "bf16" else 64, 999, 3, "zigzag", True, seed=308)
+    r = 1
+    ri, do_local, o_dev, lse_dev, kw, ref = c.rank(r)
+    run = c.run_gpu(r, ri, do_local, o_dev, lse_dev, kw)
+    ws = torch.empty(cpr.cp_ring_attn_bwd_workspace_size(c.B, c.H, c.lq), dtype=torch.uint8, device="cuda")
+    cpr.cp_ring_attn_bwd_prep(o_dev, do_local, lse_dev, ri.q_pos, True, ws)
+    dq = torch.zeros(ri.q_local.shape, dtype=torch.float32, device="cuda")
+    dk = torch.zeros(ri.k_ring.shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(ri.v_ring.shape, dtype=torch.float32, device="cuda")
+    for t in range(c.cp):
+        src = (r - t) % c.cp
+        sl = slice(src * c.lq, (src + 1) * c.lq)
+        dk_blk = dk[:, :, sl].contiguous()
+        dv_blk = dv[:, :, sl].contiguous()
+        cpr.cp_ring_attn_bwd_step(ri.q_local, do_local, ri.k_ring[:, :, sl], ri.v_ring[:, :, sl], ri.ring_pos[sl],
+                                  0.0, ws, dq, dk_blk, dv_blk)
+        dk[:, :, sl] = dk_blk
+        dv[:, :, sl] = dv_blk
+    torch.cuda.synchronize()
+    step = (dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy())
+    for g, rg, rf, z, n in zip(step, run, ref, c.zero_rows, ("dQ", "dK", "dV")):
+        check(g, rf, dtype, f"step_{dtype} {n}", z)
+        tol = 1e-6 if dtype == "f32" else 1e-5
+        assert np.abs(g - rg).max() <= tol * np.abs(rf).max(), n
