@@ -192,6 +192,65 @@ def layout_balance(args, cpr, di, torch, np, w, gen_slice, lay_codes):
                       "data": "synthetic: seeded N(0,1) draws per (tensor, b, h) slice"}), flush=True)
 
 
+def bench_backward(args, cpr, di, torch, np, w, gen_slice, lay_codes):
+    """Time one rank's backward ring pass: preprocessing, dQ over every block, the rank's share of every
+    block's dK and dV. Inputs: the same seeded Q, K, V as the forward measurement plus a seeded dO; O and
+    LSE from the library's own forward pass (timing only, nothing is checked here)."""
+    rank = w.ranks[0] if args.rank is None else args.rank
+    lay = lay_codes[w.layout]
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    nat = {t: di.upload(lambda b, h, t=t: gen_slice(w, t, b, h), w.B, w.H, w.S, w.D, tdt) for t in ("q", "k", "v", "do")}
+    tok, pos = di.layout_arrays(w.S, w.cp, lay)
+    ri = di.prepare_rank(nat["q"], nat["k"], nat["v"], w.S, w.cp, lay, rank, tok, pos)
+    do_local = di.gather(nat["do"], w.S, tok[rank * ri.lq:(rank + 1) * ri.lq])
+    del nat
+    o = torch.empty_like(ri.q_local)
+    lse = torch.empty(ri.q_local.shape[:3], dtype=torch.float32, device="cuda")
+    cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, w.causal, 0.0, o, lse)
+    dq = torch.empty(ri.q_local.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(ri.k_ring.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(ri.v_ring.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(cpr.cp_ring_attn_bwd_workspace_size(w.B, w.H, ri.lq), dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    pairs = allowed_pairs(w, ri.s_pad, ri.lq, ri.q_pos.cpu().numpy(), ri.ring_pos.cpu().numpy())
+    # FlashAttention convention: the backward is 2.5 forward passes (S recomputed, dP, dV, dQ, dK)
+    flop = 10.0 * w.B * w.H * w.D * pairs
+    stream = torch.cuda.current_stream()
+
+    def step():
+        cpr.cp_ring_attn_bwd_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, o, do_local,
+                                 lse, w.causal, 0.0, dq, dk, dv, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    value = flop / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    line = {
+        "metric": "per-rank ring-attention backward TFLOP/s (10*D flop per allowed pair); % of bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic: seeded N(0,1) draws per (tensor, b, h) slice, dO included",
+        "pct_of_peak": round(100.0 * value / peak, 2),
+        "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "D": w.D, "seq_len": w.S,
+                   "cp_size": w.cp, "layout": w.layout, "rank": rank, "causal": w.causal, "local_queries": ri.lq,
+                   "allowed_pairs_per_bh": pairs},
+        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(value, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(value / peak, 4), "traffic": None,
+                     "kernel": "bwd_prep + bwd_dq_kernel + bwd_dkv_kernel (one call)", "kernel_ms": round(ms, 4),
+                     "flop_per_launch": flop},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -204,6 +263,9 @@ def main():
     ap.add_argument("--layout-balance", action="store_true",
                     help="time every rank of the 32k-token causal sequence under the contiguous, zigzag and striped "
                          "layouts (one JSON line) instead of the default measurement")
+    ap.add_argument("--pass", dest="which", choices=("forward", "backward"), default="forward",
+                    help="backward: time the rank's backward ring pass (cp_ring_attn_bwd_run) on the same workload "
+                         "instead of the forward pass")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -240,6 +302,9 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if args.which == "backward":
+        bench_backward(args, cpr, di, torch, np, w, gen_slice, LAY_CODES)
+        return
     rank = w.ranks[0] if args.rank is None else args.rank
     lay = LAY_CODES[w.layout]
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
