@@ -310,7 +310,7 @@ cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, i
 
 size_t cp_ring_attn_bwd_workspace_size(int32_t B, int32_t H, int32_t Lq) {
   if (B < 1 || H < 1 || Lq < 1 || Lq > CPR_MAX_SEQ) return 0;
-  return round256((size_t)B * H * Lq * 8) + round256((size_t)Lq * 8);
+  return 2 * round256((size_t)B * H * Lq * 4) + round256((size_t)Lq * 8);
 }
 
 static cpr_status check_bwd_workspace(int32_t B, int32_t H, int32_t Lq, const void* ws, size_t bytes) {
@@ -320,10 +320,13 @@ static cpr_status check_bwd_workspace(int32_t B, int32_t H, int32_t Lq, const vo
   return CPR_OK;
 }
 
-static void bwd_workspace(void* ws, int32_t B, int32_t H, int32_t Lq, float2** qinfo, int2** qwin) {
+// workspace: lse2 [B*H*Lq] float, dvec [B*H*Lq] float, qwin [Lq] int2, each 256-byte aligned
+static void bwd_workspace(void* ws, int32_t B, int32_t H, int32_t Lq, float** lse2, float** dvec, int2** qwin) {
   char* w = static_cast<char*>(ws);
-  *qinfo = reinterpret_cast<float2*>(w);
-  *qwin = reinterpret_cast<int2*>(w + round256((size_t)B * H * Lq * 8));
+  const size_t plane = round256((size_t)B * H * Lq * 4);
+  *lse2 = reinterpret_cast<float*>(w);
+  *dvec = reinterpret_cast<float*>(w + plane);
+  *qwin = reinterpret_cast<int2*>(w + 2 * plane);
 }
 
 static cpr_status check_grad(const char* name, const float* p) {
@@ -363,7 +366,7 @@ cpr_status cp_ring_attn_bwd_prep(int32_t dtype, int32_t B, int32_t H, int32_t D,
   a.kw_hi = ext ? ext->kw_hi : nullptr;
   a.causal = causal ? 1 : 0;
   a.B = B; a.H = H; a.D = D; a.Lq = Lq;
-  bwd_workspace(workspace, B, H, Lq, &a.qinfo, &a.qwin);
+  bwd_workspace(workspace, B, H, Lq, &a.lse2, &a.dvec, &a.qwin);
   return hip_status(launch_bwd_prep(dtype == CPR_BF16, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_bwd_prep");
 }
 
@@ -376,10 +379,11 @@ static BwdArgs make_bwd_args(int32_t B, int32_t H, int32_t D, int32_t H_kv, cons
   a.k = k->data; a.k_sb = k->stride_b; a.k_sh = k->stride_h; a.k_sl = k->stride_l;
   a.v = v->data; a.v_sb = v->stride_b; a.v_sh = v->stride_h; a.v_sl = v->stride_l;
   a.kv_pos = kv_pos;
-  float2* qinfo;
+  float *lse2, *dvec;
   int2* qwin;
-  bwd_workspace(workspace, B, H, Lq, &qinfo, &qwin);
-  a.qinfo = qinfo;
+  bwd_workspace(workspace, B, H, Lq, &lse2, &dvec, &qwin);
+  a.lse2 = lse2;
+  a.dvec = dvec;
   a.qwin = qwin;
   a.B = B; a.H = H; a.H_kv = H_kv > 0 ? H_kv : H; a.D = D; a.Lq = Lq; a.Lk = Lk;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)D);

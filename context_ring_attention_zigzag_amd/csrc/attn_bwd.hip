@@ -15,23 +15,30 @@
 // window, pads never attended.
 //
 // Mapping to the hardware:
-//  * a preprocessing pass turns (O, dO, LSE) into per-row {LSE * log2(e),
-//    Dvec} and the positions into a per-query allowed window {lo, hi};
+//  * a preprocessing pass turns (O, dO, LSE) into per-row lse2 = LSE * log2(e)
+//    and Dvec, and the positions into a per-query allowed window {lo, hi};
+//  * every streamed tile is 32 rows, stored once in LDS, row-major with a
+//    16-byte-chunk XOR swizzle chosen so that both access patterns are free of
+//    bank conflicts: the row reads of an A operand (16 lanes, 16 rows, one
+//    chunk) and the transposed reads (ds_read_b64_tr_b16: 16 lanes, 4 rows, two
+//    chunks) that give the tile's transpose as an A operand;
 //  * the dQ kernel: a workgroup owns 128 queries of one (b, h), each wave 32 of
 //    them with Q and dO resident in VGPRs in the B-operand layout of
 //    v_mfma_f32_32x32x16_bf16. Keys stream through LDS in tiles of 32 with
-//    direct buffer->LDS loads, double-buffered: K twice (rows with a chunk
-//    swizzle for S^T = K Q^T; 4-key x 32-column sub-blocks for the transposed
-//    reads that give K^T), V once (rows, for dP^T = V dO^T). A lane then holds
-//    one query and 16 keys of a 32x32 block, so P^T and dS^T are lane-local
-//    and leave the accumulators already in the B-operand layout of
-//    dQ^T += K^T dS^T (v_cvt_pk_bf16_f32, round to nearest even);
-//  * the dK/dV kernel is the mirror image: a workgroup owns 128 keys of one
-//    (b, kv head), each wave 32 keys with K and V resident; queries stream in
-//    tiles of 32 (Q and dO, rows and sub-blocks, with their {lse2, Dvec} and
-//    windows), for every query head of the grouped-query group; S = Q K^T and
-//    dP = dO V^T give one key and 16 queries per lane, and dV^T += dO^T P,
-//    dK^T += Q^T dS take dO^T and Q^T from transposed LDS reads;
+//    direct buffer->LDS loads, double-buffered. S^T = K Q^T and dP^T = V dO^T
+//    put one query and 16 keys in each lane, so P^T and dS^T are lane-local and
+//    leave the accumulators already in the B-operand layout of
+//    dQ^T += K^T dS^T (v_cvt_pk_bf16_f32, round to nearest even); two
+//    workgroups share a CU;
+//  * the dK/dV kernel: a workgroup owns 64 keys of one (b, kv head) as two
+//    pairs of waves, 32 keys per pair, and streams query tiles (Q, dO, lse2,
+//    Dvec, windows) of every query head of the grouped-query group through
+//    three LDS buffers. The two waves of a pair split the work of each tile:
+//    role A computes S = Q K^T and P (masked) and dV^T += dO^T P with K
+//    resident; role B, one tile behind, computes dP = dO V^T and dS = P * (dP -
+//    Dvec) with P handed over through LDS in float32, and dK^T += Q^T dS with V
+//    resident. Each wave then holds half the resident operands and
+//    accumulators, and two workgroups share a CU;
 //  * both kernels classify the streamed tiles against the rows they own from
 //    position ranges (skip / full / masked) and walk an ordered list of the
 //    kept ones, as the forward kernel does; the grid keeps the workgroups of
@@ -46,83 +53,87 @@ namespace {
 
 using namespace mfma;
 
-constexpr int kT = 32;                    // rows per streamed tile
-constexpr int kNW = 4;                    // waves per workgroup, 32 owned rows each
-constexpr int kThreads = 64 * kNW;
-constexpr int kOwn = 32 * kNW;            // rows a workgroup owns
-constexpr int kMaxTiles = 8 * kThreads;   // tiles classified per segment
-constexpr int kListPad = 2;               // end markers after the last kept tile
+constexpr int kT = 32;        // rows per streamed tile
+constexpr int kListPad = 2;   // end markers after the last kept tile
 
 template <int D>
 struct BCfg {
-  static constexpr int kKSteps = D / 16;      // MFMA steps over the head dim
-  static constexpr int kDTiles = D / 32;      // 32-row tiles of a transposed gradient
-  static constexpr int kChunks = D / 8;       // 16-byte chunks per row
-  static constexpr int kDq = D / 32;          // 32-column sub-blocks per 4-row group
-  static constexpr int kLoads = kT * kChunks / kThreads;   // 16-byte loads per thread per tile copy
-  static_assert(kLoads >= 1 && (kT * kChunks) % kThreads == 0, "tile/threads mismatch");
+  static constexpr int kKSteps = D / 16;   // MFMA steps over the head dim
+  static constexpr int kDTiles = D / 32;   // 32-row tiles of a transposed gradient
+  static constexpr int kChunks = D / 8;    // 16-byte chunks per row
+  static constexpr int kTileLoads = kT * kChunks / 64;   // wave loads per tile
 };
 
-// Per-thread byte offsets (within a 32-row tile of row stride `sl` elements)
-// of the 16-byte chunks this thread's wave writes to LDS chunk slots
-// (wave * kLoads + i) * 64 + lane, for the two tile layouts:
-//  rows: slot -> row slot / kChunks, physical chunk slot % kChunks holding
-//        logical chunk swz_k(row, physical);
-//  sub-blocks: slot -> sub-block slot / 16 (4 rows x 32 columns, 4-row group
-//        sb / kDq, column block sb % kDq), chunk (slot % 16) within it.
-// Element (row, col) of a sub-block tile sits at
-// ((row / 4) * kDq + col / 32) * 128 + (row % 4) * 32 + col % 32.
+// Physical 16-byte chunk of logical chunk c in row r of a streamed tile. The
+// XOR pattern is a permutation of the row's low bits: bits (r3, r1, r0, r2) for
+// D = 128; for D = 64, whose rows are half a bank sweep, a bit rotation of
+// (r >> 1) & 7. Either way 16 consecutive rows at one chunk hit 16 distinct
+// bank groups, and 4 consecutive rows at an aligned chunk pair hit 8.
 template <int D>
-__device__ __forceinline__ void tile_offsets(int wave, int lane, int64_t sl, uint32_t (&rm)[BCfg<D>::kLoads],
-                                             uint32_t (&sb)[BCfg<D>::kLoads]) {
-  using C = BCfg<D>;
-#pragma unroll
-  for (int i = 0; i < C::kLoads; ++i) {
-    const unsigned sidx = (unsigned)((wave * C::kLoads + i) * 64 + lane);
-    const unsigned r = sidx / C::kChunks;
-    rm[i] = r * (uint32_t)sl * 2u + (uint32_t)swz_k<D>((int)r, (int)(sidx % C::kChunks)) * 16u;
-    const unsigned blk = sidx >> 4, q = sidx & 15;
-    const unsigned r2 = 4 * (blk / C::kDq) + (q >> 2), ch = 4 * (blk % C::kDq) + (q & 3);
-    sb[i] = r2 * (uint32_t)sl * 2u + ch * 16u;
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (D == 128) {
+    return c ^ ((((r >> 3) & 1) << 3) | ((r & 3) << 1) | ((r >> 2) & 1));
+  } else {
+    const int k = (r >> 1) & 7;
+    return c ^ (((k & 1) << 2) | (k >> 1));
   }
 }
 
-// The wave's share of one tile copy: kLoads 16-byte loads into LDS chunk slots
-// (wave * kLoads + i) * 64 + lane of `dst`.
+// Element offset of (row r, column col) in a streamed tile.
 template <int D>
-__device__ __forceinline__ void load_tile(const i32x4& rsrc, const uint32_t (&off)[BCfg<D>::kLoads], __bf16* dst,
-                                          int wave) {
+__device__ __forceinline__ int tile_off(int r, int col) {
+  return r * D + swz<D>(r, col >> 3) * 8 + (col & 7);
+}
+
+// Byte offset, within a 32-row tile of row stride `sl` elements, of the global
+// 16-byte chunk that LDS chunk slot `sidx` of the tile holds.
+template <int D>
+__device__ __forceinline__ uint32_t dma_off(unsigned sidx, int64_t sl) {
+  constexpr int kChunks = D / 8;
+  const unsigned r = sidx / kChunks;
+  return r * (uint32_t)sl * 2u + (uint32_t)swz<D>((int)r, (int)(sidx % kChunks)) * 16u;
+}
+
+// A-operand fragments of a tile: row ql, logical chunk 2 * kk + hh (8 columns
+// of the contraction dim).
+template <int D>
+struct RowFrags {
+  int off[BCfg<D>::kKSteps];
+  __device__ __forceinline__ void init(int ql, int hh) {
 #pragma unroll
-  for (int i = 0; i < BCfg<D>::kLoads; ++i) dma_b128(rsrc, off[i], lds_addr(dst + (wave * BCfg<D>::kLoads + i) * 512));
-}
+    for (int kk = 0; kk < BCfg<D>::kKSteps; ++kk) off[kk] = tile_off<D>(ql, 16 * kk + 8 * hh);
+  }
+  __device__ __forceinline__ bf16x8 get(const __bf16* tile, int kk) const {
+    return *reinterpret_cast<const bf16x8*>(tile + off[kk]);
+  }
+};
 
-// A-operand fragment of a row tile: row `ql`, logical chunk 2 * kk + hh.
+// A-operand fragments of the transposed tile through two transposed reads:
+// lane (column d = 32 * dt + lane % 32, half hh) gets rows 16c + 4hh + {0..3}
+// and 16c + 8 + 4hh + {0..3}, the rows whose values a B operand packed from an
+// accumulator chunk c holds for k = 8 * hh + {0..7}. 16-lane group g reads row
+// 4 * hh + (gi >> 2) of its 4-row group, 4 columns at 16 * (g & 1) + 4 * (gi & 3).
+// Row r + 16 has the swizzle of row r, so chunk c = 1 sits 16 rows further.
 template <int D>
-__device__ __forceinline__ bf16x8 row_frag(const __bf16* tile, int ql, int hh, int kk) {
-  return *reinterpret_cast<const bf16x8*>(tile + ql * D + swz_k<D>(ql, 2 * kk + hh) * 8);
-}
+struct TrFrags {
+  int off[2][BCfg<D>::kDTiles];
+  __device__ __forceinline__ void init(int lane) {
+    const int r = 4 * (lane >> 5) + ((lane & 15) >> 2);
+    const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < BCfg<D>::kDTiles; ++dt) {
+      off[0][dt] = tile_off<D>(r, 32 * dt + col);
+      off[1][dt] = tile_off<D>(r + 8, 32 * dt + col);
+    }
+  }
+  __device__ __forceinline__ bf16x8 get(const __bf16* tile, int c, int dt) const {
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off[0][dt] + 16 * c * D));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off[1][dt] + 16 * c * D));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+};
 
-// A-operand fragment of the transposed tile, from the sub-block copy: lane
-// (column d = 32 * dt + lane % 32, half hh) gets rows 16c + 4hh + {0..3} and
-// 16c + 8 + 4hh + {0..3}, the rows whose values a B operand packed from the
-// accumulators (chunk c) holds for k = 8 * hh + {0..7}.
-template <int D>
-__device__ __forceinline__ bf16x8 tr_frag(const __bf16* tile_sb, int tbase, int c, int dt) {
-  constexpr int kDq = BCfg<D>::kDq;
-  const __bf16* p = tile_sb + tbase + (4 * c * kDq + dt) * 128;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 2 * kDq * 128));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// lane's base offset for tr_frag: 16-lane group g reads 4 columns of row
-// 4 * (g >> 1) + (gi >> 2) of its 4-row group, columns 16 * (g & 1) + 4 * (gi & 3)
-__device__ __forceinline__ int tr_base(int lane, int kDq) {
-  return (lane >> 5) * kDq * 128 + ((lane & 15) >> 2) * 32 + ((lane >> 4) & 1) * 16 + (lane & 3) * 4;
-}
-
-// 16 bf16 values of one 32x32 accumulator chunk c (elements 8c .. 8c+7) as a
-// B operand
+// 8 bf16 values of a 32x32 accumulator's chunk c (elements 8c .. 8c+7) as a B operand
 __device__ __forceinline__ bf16x8 pack_chunk(const float (&x)[16], int c) {
   uint32_t w4[4];
 #pragma unroll
@@ -175,7 +186,8 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdPrepArgs a) {
   for (int o = kLanes / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kLanes);
   if (row >= rows || sub != 0) return;
   const float l = a.lse[row];
-  a.qinfo[row] = make_float2(l == -INFINITY ? INFINITY : l * kLog2e, acc);
+  a.lse2[row] = l == -INFINITY ? INFINITY : l * kLog2e;
+  a.dvec[row] = acc;
   if (bh == 0) {
     const int32_t qp = a.q_pos[i];
     int32_t lo = 1, hi = 0;   // empty
@@ -190,19 +202,24 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdPrepArgs a) {
 
 // ---------------------------------------------------------------- dQ kernel
 
-template <int D>
-__global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
-  using C = BCfg<D>;
-  constexpr int kDq = C::kDq;
+constexpr int kQWaves = 4;                    // 32 queries each
+constexpr int kQThreads = 64 * kQWaves;
+constexpr int kQOwn = 32 * kQWaves;           // queries per workgroup
+constexpr int kQMaxTiles = 8 * kQThreads;     // key tiles classified per segment
 
-  __shared__ __attribute__((aligned(16))) __bf16 k_rm[2][kT * D];   // K rows (A operand of S^T)
-  __shared__ __attribute__((aligned(16))) __bf16 k_sb[2][kT * D];   // K sub-blocks (K^T fragments)
-  __shared__ __attribute__((aligned(16))) __bf16 v_rm[2][kT * D];   // V rows (A operand of dP^T)
+template <int D>
+__global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
+  using C = BCfg<D>;
+  constexpr int kLoads = C::kTileLoads / kQWaves;   // per wave per tensor
+  static_assert(kLoads >= 1 && C::kTileLoads % kQWaves == 0, "tile/waves mismatch");
+
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][kT * D];   // K tiles (S^T A operand, K^T reads)
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][kT * D];   // V tiles (dP^T A operand)
   __shared__ __attribute__((aligned(16))) int32_t pos_lds[2][64];
-  __shared__ __attribute__((aligned(8))) uint8_t flags8[kMaxTiles];
-  __shared__ uint16_t klist[kMaxTiles + kListPad];
-  __shared__ int32_t qrange[4][kNW];
-  __shared__ int32_t wcount[kNW];
+  __shared__ __attribute__((aligned(8))) uint8_t flags8[kQMaxTiles];
+  __shared__ uint16_t klist[kQMaxTiles + kListPad];
+  __shared__ int32_t qrange[4][kQWaves];
+  __shared__ int32_t wcount[kQWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -210,13 +227,13 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
   const int ql = lane & 31;
   const int hh = lane >> 5;
 
-  const int nqt = (a.Lq + kOwn - 1) / kOwn;
+  const int nqt = (a.Lq + kQOwn - 1) / kQOwn;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int bh = logical / nqt;
   const int qt = nqt - 1 - (logical - bh * nqt);
   const int b = bh / a.H;
   const int h = bh - b * a.H;
-  const int q_idx = qt * kOwn + wave * 32 + ql;
+  const int q_idx = qt * kQOwn + wave * 32 + ql;
   const bool q_in = q_idx < a.Lq;
   const int64_t srow = (int64_t)bh * a.Lq + q_idx;
 
@@ -226,13 +243,14 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
     const int2 w = a.qwin[q_idx];
     qlow = w.x;
     qlim = w.y;
-    const float2 qi = a.qinfo[srow];
-    lse2 = qi.x;
-    dvec = qi.y;
+    lse2 = a.lse2[srow];
+    dvec = a.dvec[srow];
   }
   const bool q_live = qlow <= qlim;
 
-  // bounds over the workgroup's live queries (see the forward kernel)
+  // bounds over the workgroup's live queries: the lowest and highest allowed
+  // key position any query may attend (lb_min, ub_max) and every query may
+  // attend (lb_max, ub_min)
   int lb_min, lb_max, ub_min, ub_max;
   {
     const int w0 = wave_min(q_live ? qlow : INT_MAX), w1 = wave_max(q_live ? qlow : -1);
@@ -249,7 +267,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
     ub_min = INT_MAX;
     ub_max = -1;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) {
+    for (int w = 0; w < kQWaves; ++w) {
       lb_min = min(lb_min, qrange[0][w]);
       lb_max = max(lb_max, qrange[1][w]);
       ub_min = min(ub_min, qrange[2][w]);
@@ -268,6 +286,8 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
       qf[kk] = q_in ? *reinterpret_cast<const bf16x8*>(qg + 16 * kk + 8 * hh) : __builtin_bit_cast(bf16x8, z);
       gf[kk] = q_in ? *reinterpret_cast<const bf16x8*>(gg + 16 * kk + 8 * hh) : __builtin_bit_cast(bf16x8, z);
     }
+    ready(qf);
+    ready(gf);
   }
 
   // dQ^T[d = 32 * dt + 8 * i + 4 * hh + j][query] in dqt[dt][4 * i + j]
@@ -282,10 +302,18 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
   const __bf16* kbh = static_cast<const __bf16*>(a.k) + b * a.k_sb + hk * a.k_sh;
   const __bf16* vbh = static_cast<const __bf16*>(a.v) + b * a.v_sb + hk * a.v_sh;
   const int n_kt = (a.Lk + kT - 1) / kT;
-  uint32_t k_rm_off[C::kLoads], k_sb_off[C::kLoads], v_rm_off[C::kLoads], v_sb_unused[C::kLoads];
-  tile_offsets<D>(wave, lane, a.k_sl, k_rm_off, k_sb_off);
-  tile_offsets<D>(wave, lane, a.v_sl, v_rm_off, v_sb_unused);
-  const int tb = tr_base(lane, kDq);
+  // this wave's share of a tile: LDS chunk slots (wave * kLoads + i) * 64 + lane
+  uint32_t k_off[kLoads], v_off[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const unsigned sidx = (unsigned)((wave * kLoads + i) * 64 + lane);
+    k_off[i] = dma_off<D>(sidx, a.k_sl);
+    v_off[i] = dma_off<D>(sidx, a.v_sl);
+  }
+  RowFrags<D> rowf;
+  rowf.init(ql, hh);
+  TrFrags<D> trf;
+  trf.init(lane);
 
   for (int t = 0; t < a.nblocks && ub_max >= 0; ++t) {
     int src = (a.rank - t) % a.cp;
@@ -295,11 +323,11 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
     const __bf16* kb = kbh + row0 * a.k_sl;
     const __bf16* vb = vbh + row0 * a.v_sl;
 
-    for (int seg0 = 0; seg0 < n_kt; seg0 += kMaxTiles) {
-      const int nseg = min(kMaxTiles, n_kt - seg0);
+    for (int seg0 = 0; seg0 < n_kt; seg0 += kQMaxTiles) {
+      const int nseg = min(kQMaxTiles, n_kt - seg0);
       // ---- classify the segment's key tiles: 8 lanes per tile, 4 positions each
       bar();
-      for (int base = 0; base < nseg; base += kThreads / 8) {
+      for (int base = 0; base < nseg; base += kQThreads / 8) {
         const int tt = base + (tid >> 3);
         const int g8 = tid & 7;
         int kmin = INT_MAX, kmax = -1, pad = 0;
@@ -331,7 +359,7 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
         }
       }
       bar();
-      const int nk = build_tile_list<kNW, kListPad>(flags8, nseg, klist, wcount);
+      const int nk = build_tile_list<kQWaves, kListPad>(flags8, nseg, klist, wcount);
       bar();
       if (nk == 0) continue;
 
@@ -341,9 +369,11 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
         const uint32_t rows = (uint32_t)min(kT, a.Lk - r0);
         const i32x4 rk = make_rsrc(kb + (int64_t)r0 * a.k_sl, rows * (uint32_t)a.k_sl * 2u);
         const i32x4 rv = make_rsrc(vb + (int64_t)r0 * a.v_sl, rows * (uint32_t)a.v_sl * 2u);
-        load_tile<D>(rk, k_rm_off, &k_rm[slot][0], wave);
-        load_tile<D>(rk, k_sb_off, &k_sb[slot][0], wave);
-        load_tile<D>(rv, v_rm_off, &v_rm[slot][0], wave);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+          dma_b128(rk, k_off[i], lds_addr(&k_lds[slot][(wave * kLoads + i) * 512]));
+          dma_b128(rv, v_off[i], lds_addr(&v_lds[slot][(wave * kLoads + i) * 512]));
+        }
         if (wave == 0) dma_b32(make_rsrc(posb + r0, rows * 4u), (uint32_t)lane * 4u, lds_addr(&pos_lds[slot][0]));
       };
 
@@ -355,15 +385,17 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
         vm_wait<0>();
         bar();   // tile u is in LDS; every wave is done with buffer (u + 1) & 1
         if (u + 1 < nk) issue(en & 0x7fff, slot ^ 1);
+        const __bf16* kl = &k_lds[slot][0];
+        const __bf16* vl = &v_lds[slot][0];
 
         // S^T = K Q^T and dP^T = V dO^T for this tile's 32 keys
         f32x16 st = {}, pt = {};
 #pragma unroll
         for (int kk = 0; kk < C::kKSteps; ++kk)
-          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(&k_rm[slot][0], ql, hh, kk), qf[kk], st, 0, 0, 0);
+          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowf.get(kl, kk), qf[kk], st, 0, 0, 0);
 #pragma unroll
         for (int kk = 0; kk < C::kKSteps; ++kk)
-          pt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(&v_rm[slot][0], ql, hh, kk), gf[kk], pt, 0, 0, 0);
+          pt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowf.get(vl, kk), gf[kk], pt, 0, 0, 0);
 
         // lane: query ql, keys 8 * i + 4 * hh + jj of the tile (element 4 * i + jj)
         float s[16], ds[16];
@@ -393,10 +425,10 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
         // dQ^T += K^T dS^T
 #pragma unroll
         for (int dt = 0; dt < C::kDTiles; ++dt)
-          dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(&k_sb[slot][0], tb, 0, dt), d0, dqt[dt], 0, 0, 0);
+          dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(kl, 0, dt), d0, dqt[dt], 0, 0, 0);
 #pragma unroll
         for (int dt = 0; dt < C::kDTiles; ++dt)
-          dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(&k_sb[slot][0], tb, 1, dt), d1, dqt[dt], 0, 0, 0);
+          dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(kl, 1, dt), d1, dqt[dt], 0, 0, 0);
       }
     }
   }
@@ -423,36 +455,44 @@ __global__ void __launch_bounds__(kThreads, 2) bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------- dK/dV kernel
 
-template <int D>
-__global__ void __launch_bounds__(kThreads, D == 128 ? 1 : 2) bwd_dkv_kernel(BwdArgs a) {
-  using C = BCfg<D>;
-  constexpr int kDq = C::kDq;
+constexpr int kKvWaves = 4;                   // waves 0, 1: role A of pairs 0, 1; waves 2, 3: role B
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int kKvOwn = 64;                    // keys per workgroup, 32 per pair
+constexpr int kKvMaxTiles = 8 * kKvThreads;   // query tiles classified per segment
 
-  __shared__ __attribute__((aligned(16))) __bf16 q_rm[2][kT * D];   // Q rows (A operand of S)
-  __shared__ __attribute__((aligned(16))) __bf16 q_sb[2][kT * D];   // Q sub-blocks (Q^T fragments)
-  __shared__ __attribute__((aligned(16))) __bf16 g_rm[2][kT * D];   // dO rows (A operand of dP)
-  __shared__ __attribute__((aligned(16))) __bf16 g_sb[2][kT * D];   // dO sub-blocks (dO^T fragments)
-  __shared__ __attribute__((aligned(16))) float2 qi_lds[2][kT];     // {lse2, Dvec} of the tile's queries
-  __shared__ __attribute__((aligned(16))) int2 qw_lds[2][kT];       // {lo, hi} of the tile's queries
-  __shared__ __attribute__((aligned(8))) uint8_t flags8[kMaxTiles];
-  __shared__ uint16_t klist[kMaxTiles + kListPad];
-  __shared__ int32_t krange[3][kNW];
-  __shared__ int32_t wcount[kNW];
+template <int D>
+__global__ void __launch_bounds__(kKvThreads, 2) bwd_dkv_kernel(BwdArgs a) {
+  using C = BCfg<D>;
+  constexpr int kLoads = C::kTileLoads / 2;   // per wave: two waves per tensor
+  static_assert(kLoads >= 1 && C::kTileLoads % 2 == 0, "tile/waves mismatch");
+
+  __shared__ __attribute__((aligned(16))) __bf16 q_lds[3][kT * D];   // Q tiles (S A operand, Q^T reads)
+  __shared__ __attribute__((aligned(16))) __bf16 g_lds[3][kT * D];   // dO tiles (dP A operand, dO^T reads)
+  __shared__ __attribute__((aligned(16))) float l2_lds[3][64];       // lse2 of the tile's queries (32 used)
+  __shared__ __attribute__((aligned(16))) float dv_lds[3][64];       // Dvec of the tile's queries (32 used)
+  __shared__ __attribute__((aligned(16))) int2 qw_lds[3][kT];        // {lo, hi} of the tile's queries
+  __shared__ __attribute__((aligned(16))) float4 p_lds[2][2][4 * 64];   // P from role A to role B, per pair
+  __shared__ __attribute__((aligned(8))) uint8_t flags8[kKvMaxTiles];
+  __shared__ uint16_t klist[kKvMaxTiles + kListPad];
+  __shared__ int32_t krange[3][kKvWaves];
+  __shared__ int32_t wcount[kKvWaves];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool role_a = wave < 2;
+  const int pair = wave & 1;
   const int ql = lane & 31;   // key column owned by this lane
   const int hh = lane >> 5;
 
   const int64_t lk_total = (int64_t)a.nblocks * a.Lk;
-  const int nkt = (int)((lk_total + kOwn - 1) / kOwn);
+  const int nkt = (int)((lk_total + kKvOwn - 1) / kKvOwn);
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int bhk = logical / nkt;
   const int kt = logical - bhk * nkt;
   const int b = bhk / a.H_kv;
   const int hk = bhk - b * a.H_kv;
-  const int64_t k_idx = (int64_t)kt * kOwn + wave * 32 + ql;
+  const int64_t k_idx = (int64_t)kt * kKvOwn + pair * 32 + ql;
   const bool k_in = k_idx < lk_total;
   const int32_t kp = k_in ? a.kv_pos[k_idx] : -1;
 
@@ -471,49 +511,52 @@ __global__ void __launch_bounds__(kThreads, D == 128 ? 1 : 2) bwd_dkv_kernel(Bwd
     kmax = -1;
     anypad = 0;
 #pragma unroll
-    for (int w = 0; w < kNW; ++w) {
+    for (int w = 0; w < kKvWaves; ++w) {
       kmin = min(kmin, krange[0][w]);
       kmax = max(kmax, krange[1][w]);
       anypad |= krange[2][w];
     }
   }
 
-  // resident K and V (B operands): d = 16 * kk + 8 * hh + e of key k_idx
-  bf16x8 kf[C::kKSteps], vf[C::kKSteps];
+  // resident B operands: K rows (role A) or V rows (role B), d = 16 * kk + 8 * hh + e
+  bf16x8 rf[C::kKSteps];
   {
-    const __bf16* kg = static_cast<const __bf16*>(a.k) + b * a.k_sb + hk * a.k_sh + k_idx * a.k_sl;
-    const __bf16* vg = static_cast<const __bf16*>(a.v) + b * a.v_sb + hk * a.v_sh + k_idx * a.v_sl;
+    const __bf16* src = role_a ? static_cast<const __bf16*>(a.k) + b * a.k_sb + hk * a.k_sh + k_idx * a.k_sl
+                               : static_cast<const __bf16*>(a.v) + b * a.v_sb + hk * a.v_sh + k_idx * a.v_sl;
     const s16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int kk = 0; kk < C::kKSteps; ++kk) {
-      kf[kk] = k_in ? *reinterpret_cast<const bf16x8*>(kg + 16 * kk + 8 * hh) : __builtin_bit_cast(bf16x8, z);
-      vf[kk] = k_in ? *reinterpret_cast<const bf16x8*>(vg + 16 * kk + 8 * hh) : __builtin_bit_cast(bf16x8, z);
-    }
+    for (int kk = 0; kk < C::kKSteps; ++kk)
+      rf[kk] = k_in ? *reinterpret_cast<const bf16x8*>(src + 16 * kk + 8 * hh) : __builtin_bit_cast(bf16x8, z);
+    ready(rf);
   }
 
-  // dV^T and dK^T[d = 32 * dt + 8 * i + 4 * hh + j][key] in [dt][4 * i + j]
-  f32x16 dvt[C::kDTiles], dkt[C::kDTiles];
+  // dV^T (role A) or dK^T (role B) [d = 32 * dt + 8 * i + 4 * hh + j][key] in acc[dt][4 * i + j]
+  f32x16 acc[C::kDTiles];
 #pragma unroll
   for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      dvt[dt][i] = 0.f;
-      dkt[dt][i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) acc[dt][i] = 0.f;
 
   const float c2 = a.scale * kLog2e;
   const int group = a.H / a.H_kv;
   const int n_qt = (a.Lq + kT - 1) / kT;
-  uint32_t q_rm_off[C::kLoads], q_sb_off[C::kLoads], g_rm_off[C::kLoads], g_sb_off[C::kLoads];
-  tile_offsets<D>(wave, lane, a.q_sl, q_rm_off, q_sb_off);
-  tile_offsets<D>(wave, lane, a.do_sl, g_rm_off, g_sb_off);
-  const int tb = tr_base(lane, kDq);
+  // this wave's share of a query tile: Q (waves 0, 1) or dO (waves 2, 3), LDS
+  // chunk slots ((wave & 1) * kLoads + i) * 64 + lane
+  const bool load_q = wave < 2;
+  uint32_t ld_off[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i)
+    ld_off[i] = dma_off<D>((unsigned)(((wave & 1) * kLoads + i) * 64 + lane), load_q ? a.q_sl : a.do_sl);
+  RowFrags<D> rowf;
+  rowf.init(ql, hh);
+  TrFrags<D> trf;
+  trf.init(lane);
 
-  for (int seg0 = 0; seg0 < n_qt && kmax >= 0; seg0 += kMaxTiles) {
-    const int nseg = min(kMaxTiles, n_qt - seg0);
+  for (int seg0 = 0; seg0 < n_qt && kmax >= 0; seg0 += kKvMaxTiles) {
+    const int nseg = min(kKvMaxTiles, n_qt - seg0);
     // ---- classify the segment's query tiles: 8 lanes per tile, 4 queries each
     bar();
-    for (int base = 0; base < nseg; base += kThreads / 8) {
+    for (int base = 0; base < nseg; base += kKvThreads / 8) {
       const int tt = base + (tid >> 3);
       const int g8 = tid & 7;
       int lbmin = INT_MAX, lbmax = -1, ubmin = INT_MAX, ubmax = -1, dead = 0;
@@ -554,7 +597,7 @@ __global__ void __launch_bounds__(kThreads, D == 128 ? 1 : 2) bwd_dkv_kernel(Bwd
       }
     }
     bar();
-    const int nk = build_tile_list<kNW, kListPad>(flags8, nseg, klist, wcount);
+    const int nk = build_tile_list<kKvWaves, kListPad>(flags8, nseg, klist, wcount);
     bar();
     if (nk == 0) continue;
     const int nitems = nk * group;   // (kept tile, query head of the group), head fastest
@@ -565,49 +608,38 @@ __global__ void __launch_bounds__(kThreads, D == 128 ? 1 : 2) bwd_dkv_kernel(Bwd
       const int j = klist[u] & 0x7fff;
       const int q0 = (seg0 + j) * kT;
       const uint32_t rows = (uint32_t)min(kT, a.Lq - q0);
-      const __bf16* qb = static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)q0 * a.q_sl;
-      const __bf16* gb = static_cast<const __bf16*>(a.dout) + b * a.do_sb + h * a.do_sh + (int64_t)q0 * a.do_sl;
-      const i32x4 rq = make_rsrc(qb, rows * (uint32_t)a.q_sl * 2u);
-      const i32x4 rg = make_rsrc(gb, rows * (uint32_t)a.do_sl * 2u);
-      load_tile<D>(rq, q_rm_off, &q_rm[slot][0], wave);
-      load_tile<D>(rq, q_sb_off, &q_sb[slot][0], wave);
-      load_tile<D>(rg, g_rm_off, &g_rm[slot][0], wave);
-      load_tile<D>(rg, g_sb_off, &g_sb[slot][0], wave);
+      const __bf16* base = load_q
+          ? static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)q0 * a.q_sl
+          : static_cast<const __bf16*>(a.dout) + b * a.do_sb + h * a.do_sh + (int64_t)q0 * a.do_sl;
+      const i32x4 rs = make_rsrc(base, rows * (uint32_t)(load_q ? a.q_sl : a.do_sl) * 2u);
+      __bf16* dst = load_q ? &q_lds[slot][0] : &g_lds[slot][0];
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) dma_b128(rs, ld_off[i], lds_addr(dst + ((wave & 1) * kLoads + i) * 512));
+      const int64_t qrow = (int64_t)(b * a.H + h) * a.Lq + q0;
       if (wave == 0) {
-        const float2* qi = a.qinfo + ((int64_t)(b * a.H + h) * a.Lq + q0);
-        dma_b32(make_rsrc(qi, rows * 8u), (uint32_t)lane * 4u, lds_addr(&qi_lds[slot][0]));
+        dma_b32(make_rsrc(a.lse2 + qrow, rows * 4u), (uint32_t)lane * 4u, lds_addr(&l2_lds[slot][0]));
       } else if (wave == 1) {
+        dma_b32(make_rsrc(a.dvec + qrow, rows * 4u), (uint32_t)lane * 4u, lds_addr(&dv_lds[slot][0]));
+      } else if (wave == 2) {
         dma_b32(make_rsrc(a.qwin + q0, rows * 8u), (uint32_t)lane * 4u, lds_addr(&qw_lds[slot][0]));
       }
     };
 
-    issue(0, 0);
-    for (int it = 0; it < nitems; ++it) {
-      const int u = it / group;
-      const int e = __builtin_amdgcn_readfirstlane((int)klist[u]);
-      const int slot = it & 1;
-      vm_wait<0>();
-      bar();
-      if (it + 1 < nitems) issue(it + 1, slot ^ 1);
-
-      // S = Q K^T and dP = dO V^T for the tile's 32 queries
-      f32x16 sa = {}, pa = {};
+    // role A, item `it` in buffer `slot`
+    auto step_a = [&](int it, int slot) __attribute__((always_inline)) {
+      const int e = __builtin_amdgcn_readfirstlane((int)klist[it / group]);
+      const __bf16* qt_l = &q_lds[slot][0];
+      f32x16 sa = {};
 #pragma unroll
       for (int kk = 0; kk < C::kKSteps; ++kk)
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(&q_rm[slot][0], ql, hh, kk), kf[kk], sa, 0, 0, 0);
-#pragma unroll
-      for (int kk = 0; kk < C::kKSteps; ++kk)
-        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag<D>(&g_rm[slot][0], ql, hh, kk), vf[kk], pa, 0, 0, 0);
-
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowf.get(qt_l, kk), rf[kk], sa, 0, 0, 0);
       // lane: key ql, queries 8 * i + 4 * hh + jj of the tile (element 4 * i + jj)
-      float p[16], ds[16];
+      float p[16];
       const int remq = a.Lq - (seg0 + (e & 0x7fff)) * kT - 4 * hh;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float4 x0 = *reinterpret_cast<const float4*>(&qi_lds[slot][8 * i + 4 * hh]);
-        const float4 x1 = *reinterpret_cast<const float4*>(&qi_lds[slot][8 * i + 4 * hh + 2]);
-        const float l2[4] = {x0.x, x0.z, x1.x, x1.z};
-        const float dv[4] = {x0.y, x0.w, x1.y, x1.w};
+        const float4 l2 = *reinterpret_cast<const float4*>(&l2_lds[slot][8 * i + 4 * hh]);
+        const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
         bool ok[4] = {true, true, true, true};
         if (e & 0x8000) {
           const int4 w0 = *reinterpret_cast<const int4*>(&qw_lds[slot][8 * i + 4 * hh]);
@@ -619,65 +651,98 @@ __global__ void __launch_bounds__(kThreads, D == 128 ? 1 : 2) bwd_dkv_kernel(Bwd
         }
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float e2 = __builtin_amdgcn_exp2f(fmaf(sa[4 * i + jj], c2, -l2[jj]));
+          const float e2 = __builtin_amdgcn_exp2f(fmaf(sa[4 * i + jj], c2, -l2v[jj]));
           p[4 * i + jj] = ok[jj] ? e2 : 0.f;
-          ds[4 * i + jj] = p[4 * i + jj] * (pa[4 * i + jj] - dv[jj]);
         }
+        p_lds[it & 1][pair][i * 64 + lane] = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
       }
       const bf16x8 p0 = pack_chunk(p, 0), p1 = pack_chunk(p, 1);
-      const bf16x8 d0 = pack_chunk(ds, 0), d1 = pack_chunk(ds, 1);
+      const __bf16* gt_l = &g_lds[slot][0];
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(gt_l, 0, dt), p0, acc[dt], 0, 0, 0);
+#pragma unroll
+      for (int dt = 0; dt < C::kDTiles; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(gt_l, 1, dt), p1, acc[dt], 0, 0, 0);
+    };
 
-      // dV^T += dO^T P and dK^T += Q^T dS
+    // role B, item `it` in buffer `slot` (role A wrote its P one barrier earlier)
+    auto step_b = [&](int it, int slot) __attribute__((always_inline)) {
+      const __bf16* gt_l = &g_lds[slot][0];
+      f32x16 pa = {};
+#pragma unroll
+      for (int kk = 0; kk < C::kKSteps; ++kk)
+        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowf.get(gt_l, kk), rf[kk], pa, 0, 0, 0);
+      float ds[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 dv = *reinterpret_cast<const float4*>(&dv_lds[slot][8 * i + 4 * hh]);
+        const float dvv[4] = {dv.x, dv.y, dv.z, dv.w};
+        const float4 pv = p_lds[it & 1][pair][i * 64 + lane];
+        const float pp[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) ds[4 * i + jj] = pp[jj] * (pa[4 * i + jj] - dvv[jj]);
+      }
+      const bf16x8 d0 = pack_chunk(ds, 0), d1 = pack_chunk(ds, 1);
+      const __bf16* qt_l = &q_lds[slot][0];
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt)
-        dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(&g_sb[slot][0], tb, 0, dt), p0, dvt[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(qt_l, 0, dt), d0, acc[dt], 0, 0, 0);
 #pragma unroll
       for (int dt = 0; dt < C::kDTiles; ++dt)
-        dvt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(&g_sb[slot][0], tb, 1, dt), p1, dvt[dt], 0, 0, 0);
-#pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt)
-        dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(&q_sb[slot][0], tb, 0, dt), d0, dkt[dt], 0, 0, 0);
-#pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt)
-        dkt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<D>(&q_sb[slot][0], tb, 1, dt), d1, dkt[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(qt_l, 1, dt), d1, acc[dt], 0, 0, 0);
+    };
+
+    issue(0, 0);
+    int slot = 0;   // buffer of item it; item it - 1 sits in (slot + 2) % 3
+    for (int it = 0; it <= nitems; ++it) {
+      vm_wait<0>();
+      bar();   // item it is in LDS, P of item it - 1 is written, buffer (it + 1) % 3 is free
+      const int nslot = slot == 2 ? 0 : slot + 1;
+      if (it + 1 < nitems) issue(it + 1, nslot);
+      if (role_a) {
+        if (it < nitems) step_a(it, slot);
+      } else if (it >= 1) {
+        step_b(it - 1, slot == 0 ? 2 : slot - 1);
+      }
+      slot = nslot;
     }
   }
 
   if (!k_in) return;
   const int64_t krow = (int64_t)bhk * lk_total + k_idx;
-  float* dko = a.dk + krow * D;
-  float* dvo = a.dv + krow * D;
+  float* out = (role_a ? a.dv : a.dk) + krow * D;
+  const float sc = role_a ? 1.f : a.scale;
 #pragma unroll
   for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float4 xk = make_float4(a.scale * dkt[dt][4 * i + 0], a.scale * dkt[dt][4 * i + 1],
-                              a.scale * dkt[dt][4 * i + 2], a.scale * dkt[dt][4 * i + 3]);
-      float4 xv = make_float4(dvt[dt][4 * i + 0], dvt[dt][4 * i + 1], dvt[dt][4 * i + 2], dvt[dt][4 * i + 3]);
-      float4* pk = reinterpret_cast<float4*>(dko + 32 * dt + 8 * i + 4 * hh);
-      float4* pv = reinterpret_cast<float4*>(dvo + 32 * dt + 8 * i + 4 * hh);
+      float4 x = make_float4(sc * acc[dt][4 * i + 0], sc * acc[dt][4 * i + 1], sc * acc[dt][4 * i + 2],
+                             sc * acc[dt][4 * i + 3]);
+      float4* p = reinterpret_cast<float4*>(out + 32 * dt + 8 * i + 4 * hh);
       if (a.accumulate) {
-        const float4 yk = *pk, yv = *pv;
-        xk.x += yk.x; xk.y += yk.y; xk.z += yk.z; xk.w += yk.w;
-        xv.x += yv.x; xv.y += yv.y; xv.z += yv.z; xv.w += yv.w;
+        const float4 y = *p;
+        x.x += y.x;
+        x.y += y.y;
+        x.z += y.z;
+        x.w += y.w;
       }
-      *pk = xk;
-      *pv = xv;
+      *p = x;
     }
 }
 
 template <int D>
 hipError_t launch_bwd(const BwdArgs& a, int32_t do_dq, int32_t do_dkv, hipStream_t st) {
   if (do_dq) {
-    const int nqt = (a.Lq + kOwn - 1) / kOwn;
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nqt * a.B * a.H)), dim3(kThreads), 0, st, a);
+    const int nqt = (a.Lq + kQOwn - 1) / kQOwn;
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nqt * a.B * a.H)), dim3(kQThreads), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (do_dkv) {
     const int64_t lk_total = (int64_t)a.nblocks * a.Lk;
-    const int64_t nkt = (lk_total + kOwn - 1) / kOwn;
-    hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3((unsigned)(nkt * a.B * a.H_kv)), dim3(kThreads), 0, st, a);
+    const int64_t nkt = (lk_total + kKvOwn - 1) / kKvOwn;
+    hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3((unsigned)(nkt * a.B * a.H_kv)), dim3(kKvThreads), 0, st, a);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -51,9 +51,8 @@ __global__ void __launch_bounds__(256) bwd_dq_f32_kernel(BwdArgs a) {
     const int2 w = a.qwin[row];
     lo = w.x;
     hi = w.y;
-    const float2 qi = a.qinfo[srow];
-    lse2 = qi.x;
-    dvec = qi.y;
+    lse2 = a.lse2[srow];
+    dvec = a.dvec[srow];
   }
 
   const float* qg = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)row * a.q_sl + d0;
@@ -116,7 +115,7 @@ __global__ void __launch_bounds__(256) bwd_dkv_f32_kernel(BwdArgs a) {
   constexpr int DS = D / kLanesPerRow;
   __shared__ float qs[kTile][D];
   __shared__ float gs[kTile][D];
-  __shared__ float2 qis[kTile];
+  __shared__ float2 qis[kTile];   // {lse2, dvec}
   __shared__ int2 qws[kTile];
 
   const int tid = threadIdx.x;
@@ -147,7 +146,7 @@ __global__ void __launch_bounds__(256) bwd_dkv_f32_kernel(BwdArgs a) {
     const int h = hk * group + gi;
     const float* qg = static_cast<const float*>(a.q) + b * a.q_sb + h * a.q_sh;
     const float* gg = static_cast<const float*>(a.dout) + b * a.do_sb + h * a.do_sh;
-    const float2* qi = a.qinfo + (int64_t)(b * a.H + h) * a.Lq;
+    const int64_t qrow0 = (int64_t)(b * a.H + h) * a.Lq;
     for (int i0 = 0; i0 < a.Lq; i0 += kTile) {
       __syncthreads();
       for (int e = tid; e < kTile * D; e += 256) {
@@ -158,7 +157,8 @@ __global__ void __launch_bounds__(256) bwd_dkv_f32_kernel(BwdArgs a) {
       }
       if (tid < kTile) {
         const bool ok = i0 + tid < a.Lq;
-        qis[tid] = ok ? qi[i0 + tid] : make_float2(INFINITY, 0.f);
+        qis[tid] = ok ? make_float2(a.lse2[qrow0 + i0 + tid], a.dvec[qrow0 + i0 + tid])
+                      : make_float2(INFINITY, 0.f);
         qws[tid] = ok ? a.qwin[i0 + tid] : make_int2(1, 0);
       }
       __syncthreads();

@@ -40,9 +40,9 @@ struct AttnArgs {
   int32_t load_state, finalize;
 };
 
-// Backward pass. Preprocessing, per query row: qinfo = {LSE in log2 units (+inf
-// for a row that attends no key), rowsum(dO * O)}; per query: qwin = {lo, hi},
-// the key positions it may attend (empty when lo > hi).
+// Backward pass. Preprocessing, per query row: lse2 = LSE in log2 units (+inf
+// for a row that attends no key) and dvec = rowsum(dO * O); per query: qwin =
+// {lo, hi}, the key positions it may attend (empty when lo > hi).
 struct BwdPrepArgs {
   const void* o; int64_t o_sb, o_sh, o_sl;
   const void* dout; int64_t do_sb, do_sh, do_sl;
@@ -50,7 +50,8 @@ struct BwdPrepArgs {
   const int32_t* q_pos; const int32_t* kw_lo; const int32_t* kw_hi;
   int32_t causal;
   int32_t B, H, D, Lq;
-  float2* qinfo;                        // [B, H, Lq]
+  float* lse2;                          // [B, H, Lq]
+  float* dvec;                          // [B, H, Lq]
   int2* qwin;                           // [Lq]
 };
 
@@ -65,7 +66,8 @@ struct BwdArgs {
   const void* k; int64_t k_sb, k_sh, k_sl;
   const void* v; int64_t v_sb, v_sh, v_sl;
   const int32_t* kv_pos;
-  const float2* qinfo;
+  const float* lse2;
+  const float* dvec;
   const int2* qwin;
   int32_t B, H, H_kv, D, Lq, Lk;
   int32_t nblocks, rank, cp;

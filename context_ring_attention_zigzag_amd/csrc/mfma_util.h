@@ -109,6 +109,19 @@ __device__ __forceinline__ void bar() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_
 template <int N>
 using ic = std::integral_constant<int, N>;
 
+// Empty asm statement reading every fragment: the compiler must have the
+// loaded values here, so it waits for their global loads at this point. Placed
+// after loading a kernel's resident operands, before its tile loop; otherwise
+// the wait lands at the first use inside the loop, where it would also wait for
+// the direct-to-LDS loads of the next tile (the hardware counts both).
+template <int N>
+__device__ __forceinline__ void ready(const bf16x8 (&x)[N]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" ::"v"(x[i]));
+#endif
+}
+
 // Ordered list of kept tiles. flags8[t] (t < nseg) holds bit 0 = kept, bit 1 =
 // needs the element mask; the list gets entry t | 0x8000 (masked) or t for
 // every kept tile in increasing t, then kPad end markers equal to nseg.

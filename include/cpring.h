@@ -258,9 +258,9 @@ cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D,
  * extensions (cpr_attn_ext) and the softmax_scale default are the forward's.
  */
 
-/* Workspace bytes of the backward pass for B*H*Lq query rows: a float2
- * {LSE * log2(e), Dvec} per row, then an int2 {lo, hi} allowed key-position
- * window per query. Returns 0 for invalid sizes. */
+/* Workspace bytes of the backward pass for B*H*Lq query rows: a float
+ * LSE * log2(e) per row, a float Dvec per row, then an int2 {lo, hi} allowed
+ * key-position window per query. Returns 0 for invalid sizes. */
 size_t cp_ring_attn_bwd_workspace_size(int32_t B, int32_t H, int32_t Lq);
 
 /*
