@@ -12,6 +12,8 @@ Pages this oracle follows (cited by title and section):
 * "Context Parallelism v.s. Sequence Parallelism (Megatron-LM)"
   (orangingq.tistory.com), sections "Context Parallelism (CP)" and
   "Implementation quirk: symmetric chunk assignment".
+* the Megatron page's "Implementation quirk" also fixes that rotary position
+  embeddings take global positions (``oracle/rope.py``);
 * "Sequence Parallelism and Ring Attention" (aiunderstanding.org), sections
   "Deep dive", "Technical insight", "The future of sequence parallelism and
   ring attention" (striped layout) and the FAQ.
@@ -21,6 +23,7 @@ than itself (brute force, a library routine, closed forms, the pages' cp=4
 table). No function is "parity unpinned".
 """
 
+from .rope import HALF, INTERLEAVED, rope, rope_pairs  # noqa: F401
 from .ring_attention import (  # noqa: F401
     CONTIGUOUS,
     STRIPED,

@@ -712,3 +712,72 @@ def test_planted_wrong_kv_head_group_is_caught(monkeypatch):
     monkeypatch.setattr(ora, "kv_head", lambda h, n_h, n_kv: h % n_kv)
     with pytest.raises(AssertionError):
         test_backward_vs_torch_autograd(True, 2)
+
+
+# ----------------------------------------------------------------- RoPE pins
+
+def test_rope_d2_is_complex_rotation():
+    """D = 2: the pair (a, b) as a + ib is multiplied by exp(i * pos) (theta_0 = 1), numpy's complex exp."""
+    x = rnd((1, 1, 7, 2), 140)
+    pos = np.array([0, 1, 2, 5, 100, 12345, 999999])
+    got = oracle.rope(x, pos)
+    z = (x[..., 0] + 1j * x[..., 1]) * np.exp(1j * pos.astype(np.float64))
+    np.testing.assert_allclose(got[..., 0], z.real, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[..., 1], z.imag, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("style", [oracle.INTERLEAVED, oracle.HALF])
+def test_rope_preserves_pair_norms_and_is_identity_at_zero(style):
+    x = rnd((2, 3, 9, 16), 141)
+    pos = np.array([0, 3, 7, 64, 1000, 65535, 131071, 1048575, -1])
+    y = oracle.rope(x, pos, style=style)
+    a, b = oracle.rope_pairs(16, style)
+    np.testing.assert_allclose(y[..., a] ** 2 + y[..., b] ** 2, x[..., a] ** 2 + x[..., b] ** 2, rtol=1e-12, atol=0)
+    np.testing.assert_array_equal(y[..., 0, :], x[..., 0, :])      # position 0: no rotation
+    np.testing.assert_array_equal(y[..., -1, :], x[..., -1, :])    # pad (-1): unchanged
+    assert np.abs(y[..., 1:-1, :] - x[..., 1:-1, :]).max() > 1e-3
+
+
+@pytest.mark.parametrize("style", [oracle.INTERLEAVED, oracle.HALF])
+def test_rope_scores_depend_on_relative_position_only(style):
+    """<rope(q, m), rope(k, n)> = <rope(q, m - n), k>: the property rotary embeddings exist for."""
+    d = 32
+    q, k = rnd((d,), 142), rnd((d,), 143)
+    for m, n in ((5, 2), (100, 37), (70000, 69990), (3, 3)):
+        lhs = oracle.rope(q[None, :], np.array([m]), style=style)[0] @ oracle.rope(k[None, :], np.array([n]),
+                                                                                   style=style)[0]
+        rhs = oracle.rope(q[None, :], np.array([m - n]), style=style)[0] @ k
+        assert abs(lhs - rhs) < 1e-9 * (1 + abs(rhs))
+
+
+def test_rope_half_is_interleaved_on_permuted_dims():
+    d = 8
+    x = rnd((1, 2, 5, d), 144)
+    pos = np.array([0, 1, 9, 300, 77777])
+    perm = np.empty(d, np.int64)
+    perm[0::2] = np.arange(d // 2)                 # interleaved slot 2j <- half slot j
+    perm[1::2] = np.arange(d // 2) + d // 2        # interleaved slot 2j+1 <- half slot j + D/2
+    inter = oracle.rope(x[..., perm], pos, style=oracle.INTERLEAVED)
+    half = oracle.rope(x, pos, style=oracle.HALF)
+    np.testing.assert_allclose(inter, half[..., perm], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("layout", ["zigzag", "striped"])
+def test_rope_with_global_positions_commutes_with_the_layout(layout):
+    """Rotating the natural sequence and then gathering a rank's tokens equals gathering first and rotating
+    with the rank's global position ids (Megatron page, implementation quirk); renumbering locally does not."""
+    s, cp, d = 61, 4, 8
+    x = rnd((1, 2, s, d), 145)
+    tok, pos = oracle.layout(s, cp, LAYOUTS[layout])
+    lr = len(tok) // cp
+    nat = oracle.rope(x, np.arange(s))
+    for r in range(cp):
+        lt = tok[r * lr:(r + 1) * lr]
+        real = lt < s
+        local = np.zeros((1, 2, lr, d))
+        local[:, :, real] = x[:, :, lt[real]]
+        got = oracle.rope(local, pos[r * lr:(r + 1) * lr])
+        np.testing.assert_allclose(got[:, :, real], nat[:, :, lt[real]], rtol=0, atol=1e-12)
+        if r > 0:
+            wrong = oracle.rope(local, np.where(real, np.arange(lr), -1))   # local renumbering
+            assert np.abs(wrong[:, :, real] - nat[:, :, lt[real]]).max() > 1e-3
