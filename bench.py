@@ -106,11 +106,14 @@ def cpu_baseline(w, rank: int, budget_s: float):
                       f"of {w.B * w.H}, fp64 numpy, {t_used:.1f} s of oracle time"}
 
 
-def measure_state_kernels(cpr, torch, B: int, H: int, Lq: int, D: int, out_dtype, stream, reps: int = 10):
-    """HBM throughput of the finalize and merge kernels at the workload's state shape.
+def measure_state_kernels(cpr, torch, B: int, H: int, Lq: int, D: int, out_dtype, stream, reps: int = 10,
+                          q_local=None, q_pos=None):
+    """HBM throughput of the finalize, merge and rotary-embedding kernels at the workload's local shape.
 
     Algorithmic bytes per row: finalize reads O (4D) + m, l (8) and writes O (D*esize) + LSE (4);
-    merge reads two states (8D + 16) and writes one (4D + 8).
+    merge reads two states (8D + 16) and writes one (4D + 8); the rotary embedding of the rank's queries
+    by their global positions reads and writes one row (2*D*esize) plus its position (4 bytes per row of
+    one (b, h)).
     """
     rows = B * H * Lq
     g = torch.Generator(device="cuda").manual_seed(0)
@@ -122,11 +125,14 @@ def measure_state_kernels(cpr, torch, B: int, H: int, Lq: int, D: int, out_dtype
     lse = torch.empty((B, H, Lq), device="cuda")
     esize = out.element_size()
     res = {}
-    for name, fn, nbytes in (
-            ("finalize_kernel", lambda: cpr.cp_ring_attn_finalize(o, m, l, out, lse, stream),
-             rows * (4 * D + 8 + D * esize + 4)),
-            ("merge_kernel", lambda: cpr.cp_ring_attn_merge(o, m, l, o2, m2, l2, stream),
-             rows * (8 * D + 16 + 4 * D + 8))):
+    cases = [("finalize_kernel", lambda: cpr.cp_ring_attn_finalize(o, m, l, out, lse, stream),
+              rows * (4 * D + 8 + D * esize + 4)),
+             ("merge_kernel", lambda: cpr.cp_ring_attn_merge(o, m, l, o2, m2, l2, stream),
+              rows * (8 * D + 16 + 4 * D + 8))]
+    if q_local is not None:
+        cases.append(("rope_kernel", lambda: cpr.cp_rope_apply(q_local, q_pos, out=out, stream=stream),
+                      rows * 2 * D * esize + Lq * 4))
+    for name, fn, nbytes in cases:
         fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -362,7 +368,8 @@ def main():
                 "kernel": KERNEL_NAME if w.dtype == "bf16" else "attn_f32_kernel",
                 "kernel_ms": round(kernel_ms, 4), "flop_per_launch": flop}
 
-    state_kernels = measure_state_kernels(cpr, torch, w.B, w.H, ri.lq, w.D, tdt, stream)
+    state_kernels = measure_state_kernels(cpr, torch, w.B, w.H, ri.lq, w.D, tdt, stream, q_local=ri.q_local,
+                                          q_pos=ri.q_pos)
 
     cpu = None
     if args.cpu_budget > 0:

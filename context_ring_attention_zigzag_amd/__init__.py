@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libcpring.so")
 F32, BF16 = 0, 1
 ZIGZAG, CONTIGUOUS, STRIPED = 0, 1, 2
 RUN_FUSED, RUN_STEPWISE = 0, 1
+ROPE_INTERLEAVED, ROPE_HALF = 0, 1
 OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 
 # Every symbol include/cpring.h declares.
@@ -31,7 +32,7 @@ EXPORTS = (
     "cp_padded_len", "cp_zigzag_partition", "cp_shard_gather", "cp_ring_attn_init", "cp_ring_attn_step",
     "cp_ring_attn_merge", "cp_ring_attn_finalize", "cp_ring_attn_workspace_size", "cp_ring_attn_run",
     "cp_ring_attn_step_ex", "cp_ring_attn_run_ex", "cp_ring_attn_bwd_workspace_size", "cp_ring_attn_bwd_prep",
-    "cp_ring_attn_bwd_step", "cp_ring_attn_bwd_run", "cp_status_string", "cp_last_error",
+    "cp_ring_attn_bwd_step", "cp_ring_attn_bwd_run", "cp_rope_apply", "cp_status_string", "cp_last_error",
 )
 
 
@@ -86,6 +87,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                         ctypes.c_size_t, vp, vp, vp, vp]),
         "cp_ring_attn_bwd_run": (i32, [i32, i32, i32, i32, i32, i32, pv, i32, vp, pv, pv, vp, pv, pv, vp, i32, f32,
                                        pe, vp, vp, vp, vp, ctypes.c_size_t, vp]),
+        "cp_rope_apply": (i32, [i32, i32, i32, i32, i32, pv, vp, f32, i32, vp, vp]),
         "cp_status_string": (ctypes.c_char_p, [i32]),
         "cp_last_error": (ctypes.c_char_p, []),
     }
@@ -264,3 +266,17 @@ def cp_ring_attn_bwd_run(q_local, q_pos, k_ring, v_ring, ring_pos, cp_size: int,
                                        float(softmax_scale), None if ext is None else ctypes.byref(ext), _ptr(dq),
                                        _ptr(dk), _ptr(dv), _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "cp_ring_attn_bwd_run")
+
+
+# ----------------------------------------------------- rotary embeddings
+
+def cp_rope_apply(x, pos, out=None, base: float = 10000.0, style: int = ROPE_INTERLEAVED, stream=None):
+    """Rotate x [B, H, L, D] by the global positions pos [L] (int32, -1 = pad); returns out (contiguous,
+    allocated when None; may be x itself when x is contiguous)."""
+    B, H, L, D = x.shape
+    if out is None:
+        out = torch.empty((B, H, L, D), dtype=x.dtype, device=x.device)
+    xv = view(x)
+    _check(load().cp_rope_apply(dtype_code(x), B, H, L, D, ctypes.byref(xv), _ptr(pos), float(base), int(style),
+                                _ptr(out), _stream(stream)), "cp_rope_apply")
+    return out

@@ -447,6 +447,27 @@ cpr_status cp_ring_attn_bwd_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
   return hip_status(launch_bwd(dtype, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_bwd_run");
 }
 
+cpr_status cp_rope_apply(int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t D, const cpr_view* x,
+                         const int32_t* pos, float base, int32_t style, void* out, void* stream) {
+  TRY(check_dims(dtype, B, H, D));
+  TRY(check_len("L", L));
+  TRY(check_view("x", x, dtype));
+  TRY(check_rows16("x", x, dtype));
+  if (!pos) return fail(CPR_EINVAL, "pos is NULL");
+  if (!(base > 0.f) || isinf(base)) return fail(CPR_EINVAL, "base must be positive and finite");
+  if (style != CPR_ROPE_INTERLEAVED && style != CPR_ROPE_HALF) return fail(CPR_EINVAL, "unknown rotary style %d", style);
+  if (!out) return fail(CPR_EINVAL, "out is NULL");
+  if (!aligned(out, 16)) return fail(CPR_EINVAL, "out must be 16-byte aligned");
+  RopeArgs a{};
+  a.x = x->data; a.x_sb = x->stride_b; a.x_sh = x->stride_h; a.x_sl = x->stride_l;
+  a.pos = pos;
+  a.B = B; a.H = H; a.L = L; a.D = D;
+  a.base = base;
+  a.style = style;
+  a.out = out;
+  return hip_status(launch_rope(dtype == CPR_BF16, a, static_cast<hipStream_t>(stream)), "cp_rope_apply");
+}
+
 const char* cp_status_string(int32_t status) {
   switch (status) {
     case CPR_OK: return "ok";

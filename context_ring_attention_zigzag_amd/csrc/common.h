@@ -80,6 +80,17 @@ hipError_t launch_bwd_prep(int32_t dtype_bf16, const BwdPrepArgs& a, hipStream_t
 hipError_t launch_bwd_bf16(const BwdArgs& a, int32_t do_dq, int32_t do_dkv, hipStream_t st);
 hipError_t launch_bwd_f32(const BwdArgs& a, int32_t do_dq, int32_t do_dkv, hipStream_t st);
 
+// Rotary embedding: out (contiguous [B, H, L, D]) = x rotated by pos [L].
+struct RopeArgs {
+  const void* x; int64_t x_sb, x_sh, x_sl;
+  const int32_t* pos;
+  int32_t B, H, L, D;
+  float base;
+  int32_t style;
+  void* out;
+};
+hipError_t launch_rope(int32_t dtype_bf16, const RopeArgs& a, hipStream_t st);
+
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
 

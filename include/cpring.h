@@ -316,6 +316,34 @@ cpr_status cp_ring_attn_bwd_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
                                 float* dq_local, float* dk_ring, float* dv_ring,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Pairing of the dimensions a rotary embedding rotates together. */
+typedef enum {
+  CPR_ROPE_INTERLEAVED = 0, /* pairs (2j, 2j+1) */
+  CPR_ROPE_HALF = 1         /* pairs (j, j + D/2) */
+} cpr_rope_style;
+
+/*
+ * Rotary position embedding by global position. The Megatron page
+ * ("Implementation quirk: symmetric chunk assignment") requires rotary
+ * embeddings to use each token's global position under the chunk pairing:
+ * a rank holding chunks r and 2cp-1-r rotates its tokens by those chunks'
+ * global positions, as cp_zigzag_partition's pos_ids give them, never by a
+ * local renumbering. The rotation is the standard one: pair (a_j, b_j),
+ * j = 0 .. D/2-1, becomes (a cos t - b sin t, a sin t + b cos t) with
+ * t = pos * base^(-2j/D).
+ *   x      [B,H,L,D] view of dtype (rows 16-byte aligned for float32);
+ *   pos    int32 device array [L]: the rows' global positions, -1 = pad (the
+ *          row is copied unchanged);
+ *   base   > 0 (10000 is the usual value);
+ *   style  CPR_ROPE_INTERLEAVED or CPR_ROPE_HALF;
+ *   out    contiguous [B,H,L,D] device buffer of dtype; may be x's own
+ *          memory when x is contiguous (in place).
+ * Angles are reduced modulo 2*pi in double precision; sin and cos are then
+ * taken in float32. D must be 64 or 128.
+ */
+cpr_status cp_rope_apply(int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t D, const cpr_view* x,
+                         const int32_t* pos, float base, int32_t style, void* out, void* stream);
+
 /* Static description of a status code. */
 const char* cp_status_string(int32_t status);
 

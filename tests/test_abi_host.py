@@ -247,3 +247,19 @@ def test_bwd_validation(lib):
     assert run(cp=0) == cpr.EINVAL
     assert run(rank=2) == cpr.EINVAL and "rank" in err(lib)
     assert run(dk=None) == cpr.EINVAL and "dk_ring" in err(lib)
+
+
+def test_rope_validation(lib):
+    p = fake_ptr()
+    x = view()
+
+    def call(dtype=cpr.BF16, D=128, pos=p, base=10000.0, style=cpr.ROPE_INTERLEAVED, out=p, xv=x):
+        return lib.cp_rope_apply(dtype, 1, 2, 64, D, ctypes.byref(xv), pos, base, style, out, None)
+    assert call(pos=None) == cpr.EINVAL and "pos" in err(lib)
+    assert call(base=0.0) == cpr.EINVAL and "base" in err(lib)
+    assert call(base=float("inf")) == cpr.EINVAL
+    assert call(style=7) == cpr.EINVAL and "style" in err(lib)
+    assert call(out=None) == cpr.EINVAL
+    assert call(out=fake_ptr(0x100008)) == cpr.EINVAL and "16-byte" in err(lib)
+    assert call(D=80) == cpr.EUNSUPPORTED
+    assert call(dtype=cpr.F32, xv=view(sl=130)) == cpr.EINVAL
