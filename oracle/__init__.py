@@ -43,6 +43,7 @@ from .ring_attention import (  # noqa: F401
     padded_len,
     rank_reference,
     ring_backward,
+    rows_backward,
     ring_emulation,
     ring_source,
 )

@@ -423,6 +423,46 @@ def ring_backward(q_local, k_ring, v_ring, o_local, do_local, lse_local, q_pos, 
     return dq, dk, dv
 
 
+def rows_backward(q, k, v, o, do, lse, q_pos, k_pos, causal: bool, scale=None, kw_lo=None, kw_hi=None,
+                  q_rows=None, k_rows=None):
+    """The same gradients as ``ring_backward`` for chosen rows only, fp64, one (b, h) slice.
+
+    q, o, do [Nq, D] with lse [Nq] (the saved forward results), k, v [Nk, D].
+    Returns dQ for the query rows ``q_rows`` ([len, D]) and dK, dV for the key
+    rows ``k_rows``: dQ_i = scale * sum_j dS_ij k_j, dK_j = scale * sum_i dS_ij q_i,
+    dV_j = sum_i P_ij dO_i with P_ij = exp(scale q_i.k_j - lse_i) (0 where
+    masked or lse_i = -inf) and dS_ij = P_ij (dO_i.v_j - rowsum(dO_i * O_i)).
+    Order of keys and queries is irrelevant, so no block structure is needed.
+    """
+    q, k, v, o, do, lse = (np.asarray(x, dtype=np.float64) for x in (q, k, v, o, do, lse))
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    q_pos, k_pos = np.asarray(q_pos), np.asarray(k_pos)
+    dvec = (do * o).sum(axis=-1)
+    fin = np.isfinite(lse)
+
+    def probs(qi, kj):
+        ok = allowed_mask(q_pos[qi], k_pos[kj], causal, None if kw_lo is None else np.asarray(kw_lo)[qi],
+                          None if kw_hi is None else np.asarray(kw_hi)[qi])
+        s = scale * (q[qi] @ k[kj].T)
+        return np.where(ok & fin[qi][:, None], np.exp(s - np.where(fin[qi], lse[qi], 0.0)[:, None]), 0.0)
+
+    all_q, all_k = np.arange(len(q)), np.arange(len(k))
+    dq = dk = dv = None
+    if q_rows is not None:
+        qi = np.asarray(q_rows)
+        p = probs(qi, all_k)
+        ds = _score_grad(p, do[qi] @ v.T, dvec[qi])
+        dq = scale * (ds @ k)
+    if k_rows is not None:
+        kj = np.asarray(k_rows)
+        p = probs(all_q, kj)
+        ds = _score_grad(p, do @ v[kj].T, dvec)
+        dk = scale * (ds.T @ q)
+        dv = p.T @ do
+    return dq, dk, dv
+
+
 # ---------------------------------------------------------------------------
 # Work counts (the load-balance claim of the Megatron page).
 # ---------------------------------------------------------------------------

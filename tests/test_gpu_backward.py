@@ -202,3 +202,72 @@ def test_bwd_step_equals_run(dtype):
         check(g, rf, dtype, f"step_{dtype} {n}", z)
         tol = 1e-6 if dtype == "f32" else 1e-5
         assert np.abs(g - rg).max() <= tol * np.abs(rf).max(), n
+
+
+# ----------------------------------------------------------- full-size, sampled
+
+@pytest.mark.parametrize("wl_name", ["seq32k_cp4", "longdoc_noncausal"])
+def test_bwd_full_size_sampled(wl_name):
+    """The backward at a full benchmark workload, in the launch configuration ``bench.py --pass backward`` times.
+
+    One head gets the oracle's forward O (bf16) and LSE; every other head gets O = 0 and LSE = -inf (no key
+    allowed), for which every gradient must be exactly zero. For the checked head, dQ of sampled local queries
+    and dK, dV of sampled ring keys are compared with the oracle's row-restricted backward (normwise over the
+    sampled rows, same bar as above)."""
+    from seeded_inputs import WORKLOADS, gen_slice, sample_rows
+    w = WORKLOADS[wl_name]
+    rank, h0 = w.ranks[0], 5
+    lay_c, lay_o = LAY[w.layout]
+    note(f"{wl_name}: B={w.B} H={w.H} D={w.D} S={w.S} cp={w.cp} rank={rank} checked head {h0}")
+    nat = {t: di.upload(lambda b, h, t=t: gen_slice(w, t, b, h), w.B, w.H, w.S, w.D, torch.bfloat16)
+           for t in ("q", "k", "v", "do")}
+    tok_d, pos_d = di.layout_arrays(w.S, w.cp, lay_c)
+    ri = di.prepare_rank(nat["q"], nat["k"], nat["v"], w.S, w.cp, lay_c, rank, tok_d, pos_d)
+    lq = ri.lq
+    do_local = di.gather(nat["do"], w.S, tok_d[rank * lq:(rank + 1) * lq])
+    del nat
+
+    # oracle forward of the checked head (batch 0), from the same seeded values
+    tok, pos = oracle.layout(w.S, w.cp, lay_o)
+    sl = slice(rank * lq, (rank + 1) * lq)
+
+    def host(t, idx):
+        x = gen_slice(w, t, 0, h0).astype(np.float64)
+        out = np.zeros((len(idx), w.D))
+        out[idx < w.S] = x[idx[idx < w.S]]
+        return out
+    qh, kh, vh, gh = host("q", tok[sl]), host("k", tok), host("v", tok), host("do", tok[sl])
+    o, lse = oracle.ring_emulation(qh[None, None], kh[None, None], vh[None, None], pos[sl], pos, w.cp, rank,
+                                   w.causal)
+    o_b = torch.from_numpy(o[0, 0].astype(np.float32)).to(torch.bfloat16)
+    o_dev = torch.zeros(ri.q_local.shape, dtype=torch.bfloat16, device="cuda")
+    lse_dev = torch.full(ri.q_local.shape[:3], float("-inf"), dtype=torch.float32, device="cuda")
+    o_dev[0, h0] = o_b.cuda()
+    lse_dev[0, h0] = torch.from_numpy(lse[0, 0].astype(np.float32)).cuda()
+
+    dq = torch.empty(ri.q_local.shape, dtype=torch.float32, device="cuda")
+    dk = torch.empty(ri.k_ring.shape, dtype=torch.float32, device="cuda")
+    dv = torch.empty(ri.v_ring.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(cpr.cp_ring_attn_bwd_workspace_size(w.B, w.H, lq), dtype=torch.uint8, device="cuda")
+    cpr.cp_ring_attn_bwd_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, o_dev, do_local,
+                             lse_dev, w.causal, 0.0, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+
+    # every other head: exactly zero
+    others = [h for h in range(w.H) if h != h0]
+    for name, g in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert float(g[:, others].abs().max()) == 0.0, f"{name} of heads with no allowed key is not zero"
+        assert bool(torch.isfinite(g).all()), name
+    if w.B > 1:
+        assert float(dq[1:].abs().max()) == 0.0 and float(dk[1:].abs().max()) == 0.0
+
+    q_rows = sample_rows(lq, lq // 2 if w.layout == "zigzag" else lq, 96, seed=11)
+    k_rows = sample_rows(len(tok), lq // 2 if w.layout == "zigzag" else lq, 160, seed=12)
+    ref_q, ref_k, ref_v = oracle.rows_backward(qh, kh, vh, o_b.double().numpy(), gh,
+                                               lse[0, 0].astype(np.float32).astype(np.float64), pos[sl], pos,
+                                               w.causal, q_rows=q_rows, k_rows=k_rows)
+    got_q = dq[0, h0, torch.from_numpy(q_rows).cuda()].cpu().numpy()
+    got_k = dk[0, h0, torch.from_numpy(k_rows).cuda()].cpu().numpy()
+    got_v = dv[0, h0, torch.from_numpy(k_rows).cuda()].cpu().numpy()
+    for g, r, n in ((got_q, ref_q, "dQ"), (got_k, ref_k, "dK"), (got_v, ref_v, "dV")):
+        check(g, r, "bf16", f"{wl_name} head {h0} sampled {n}")

@@ -781,3 +781,31 @@ def test_rope_with_global_positions_commutes_with_the_layout(layout):
         if r > 0:
             wrong = oracle.rope(local, np.where(real, np.arange(lr), -1))   # local renumbering
             assert np.abs(wrong[:, :, real] - nat[:, :, lt[real]]).max() > 1e-3
+
+
+def test_rows_backward_equals_ring_backward():
+    """The row-restricted backward (used for sampled checks at full size) gives the ring backward's rows."""
+    w = small_workload("t", "f32", 1, 2, 8, 77, 3, "zigzag", True, seed=150)
+    q, k, v = (gen_tensor(w, t).astype(np.float64) for t in "qkv")
+    do = gen_tensor(w, "do").astype(np.float64)
+    tok, pos = oracle.layout(w.S, w.cp, ZZ)
+    lq = len(tok) // w.cp
+    real = tok < w.S
+
+    def gather(x, idx):
+        out = np.zeros(x.shape[:2] + (len(idx), x.shape[-1]))
+        out[:, :, idx < w.S] = x[:, :, idx[idx < w.S]]
+        return out
+    r = 2
+    sl = slice(r * lq, (r + 1) * lq)
+    qr, kr, vr, dor = gather(q, tok[sl]), gather(k, tok), gather(v, tok), gather(do, tok[sl])
+    o, lse = oracle.ring_emulation(qr, kr, vr, pos[sl], pos, w.cp, r, True)
+    dq, dk, dv = oracle.ring_backward(qr, kr, vr, o, dor, lse, pos[sl], pos, w.cp, r, True)
+    qs, ks = np.array([0, 3, lq - 1]), np.array([0, 5, 40, len(tok) - 1])
+    for h in range(2):
+        a, b, c = oracle.rows_backward(qr[0, h], kr[0, h], vr[0, h], o[0, h], dor[0, h], lse[0, h], pos[sl], pos,
+                                       True, q_rows=qs, k_rows=ks)
+        np.testing.assert_allclose(a, dq[0, h, qs], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(b, dk[0, h, ks], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(c, dv[0, h, ks], rtol=0, atol=1e-12)
+    assert real.any()
