@@ -144,6 +144,31 @@ __device__ __forceinline__ bf16x8 pack_chunk(const float (&x)[16], int c) {
   return __builtin_bit_cast(bf16x8, w4);
 }
 
+// A stream of N MFMAs whose A operands come from LDS: fragment m is read
+// kPf MFMAs ahead of its use through a ring of kPf + 1 registers, and the
+// read / MFMA order is pinned with scheduling-group barriers, so every MFMA
+// finds its operand loaded instead of waiting out the LDS latency.
+// fetch(m) returns fragment m (kReads LDS reads); mma(m, frag) issues MFMA m.
+constexpr int kPf = 4;
+template <int N, int kReads, typename Fetch, typename Mma>
+__device__ __forceinline__ void mfma_stream(Fetch&& fetch, Mma&& mma) {
+  bf16x8 fr[kPf + 1];
+#pragma unroll
+  for (int m = 0; m < kPf && m < N; ++m) fr[m] = fetch(m);
+#pragma unroll
+  for (int m = 0; m < N; ++m) {
+    if (m + kPf < N) fr[(m + kPf) % (kPf + 1)] = fetch(m + kPf);
+    mma(m, fr[m % (kPf + 1)]);
+  }
+#pragma unroll
+  for (int m = 0; m < kPf && m < N; ++m) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads, 0);
+#pragma unroll
+  for (int m = 0; m < N; ++m) {
+    if (m + kPf < N) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  }
+}
+
 // workgroup index -> logical index with the workgroups of one head on one XCD
 __device__ __forceinline__ int xcd_logical(int w, int ntiles) {
   const int xcd = w % kXcds, idx = w / kXcds;
@@ -388,14 +413,14 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
         const __bf16* kl = &k_lds[slot][0];
         const __bf16* vl = &v_lds[slot][0];
 
-        // S^T = K Q^T and dP^T = V dO^T for this tile's 32 keys
+        // S^T = K Q^T and dP^T = V dO^T for this tile's 32 keys, alternating
         f32x16 st = {}, pt = {};
-#pragma unroll
-        for (int kk = 0; kk < C::kKSteps; ++kk)
-          st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowf.get(kl, kk), qf[kk], st, 0, 0, 0);
-#pragma unroll
-        for (int kk = 0; kk < C::kKSteps; ++kk)
-          pt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowf.get(vl, kk), gf[kk], pt, 0, 0, 0);
+        mfma_stream<2 * C::kKSteps, 1>(
+            [&](int m) { return rowf.get((m & 1) ? vl : kl, m >> 1); },
+            [&](int m, const bf16x8& a) {
+              if (m & 1) pt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, gf[m >> 1], pt, 0, 0, 0);
+              else st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[m >> 1], st, 0, 0, 0);
+            });
 
         // lane: query ql, keys 8 * i + 4 * hh + jj of the tile (element 4 * i + jj)
         float s[16], ds[16];
@@ -423,12 +448,12 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
         const bf16x8 d0 = pack_chunk(ds, 0), d1 = pack_chunk(ds, 1);
 
         // dQ^T += K^T dS^T
-#pragma unroll
-        for (int dt = 0; dt < C::kDTiles; ++dt)
-          dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(kl, 0, dt), d0, dqt[dt], 0, 0, 0);
-#pragma unroll
-        for (int dt = 0; dt < C::kDTiles; ++dt)
-          dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(kl, 1, dt), d1, dqt[dt], 0, 0, 0);
+        mfma_stream<2 * C::kDTiles, 2>(
+            [&](int m) { return trf.get(kl, m / C::kDTiles, m % C::kDTiles); },
+            [&](int m, const bf16x8& a) {
+              const int dt = m % C::kDTiles;
+              dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, m < C::kDTiles ? d0 : d1, dqt[dt], 0, 0, 0);
+            });
       }
     }
   }
@@ -454,16 +479,30 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------- dK/dV kernel
-
-constexpr int kKvWaves = 4;                   // waves 0, 1: role A of pairs 0, 1; waves 2, 3: role B
+//
+// A workgroup owns 128 keys of one (b, kv head): eight waves, four pairs of 32
+// keys. Wave s (role A, K resident, dV accumulated) and wave s + 4 (role B, V
+// resident, dK accumulated) own the same keys and share SIMD s. Query tiles
+// (items) run in phases separated by workgroup barriers, and in every phase one
+// role works the matrix cores while the other works the vector ALU:
+//   phase 2k:   A: S(k) = Q(k) K^T, then dV^T += dO(k-1)^T P(k-1)   [MFMA]
+//               B: dS(k-1) = P(k-1) * (dP(k-1) - Dvec(k-1)), and the
+//                  loads of item k + 1                               [VALU]
+//   phase 2k+1: A: P(k) = 2^(S(k) c - lse2(k)), masked, handed to B
+//                  through LDS in float32                            [VALU]
+//               B: dP(k) = dO(k) V^T, then dK^T += Q(k-1)^T dS(k-1)  [MFMA]
+// Items rotate through three LDS buffers: phase 2k reads items k - 1 and k,
+// loads item k + 1 into the buffer of item k - 2, and role B waits for those
+// loads at the end of phase 2k + 1, one barrier before their first reader.
+constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
-constexpr int kKvOwn = 64;                    // keys per workgroup, 32 per pair
+constexpr int kKvOwn = 128;                   // keys per workgroup, 32 per pair
 constexpr int kKvMaxTiles = 8 * kKvThreads;   // query tiles classified per segment
 
 template <int D>
-__global__ void __launch_bounds__(kKvThreads, 2) bwd_dkv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
   using C = BCfg<D>;
-  constexpr int kLoads = C::kTileLoads / 2;   // per wave: two waves per tensor
+  constexpr int kLoads = C::kTileLoads / 2;   // per role-B wave: two waves per tensor
   static_assert(kLoads >= 1 && C::kTileLoads % 2 == 0, "tile/waves mismatch");
 
   __shared__ __attribute__((aligned(16))) __bf16 q_lds[3][kT * D];   // Q tiles (S A operand, Q^T reads)
@@ -471,7 +510,7 @@ __global__ void __launch_bounds__(kKvThreads, 2) bwd_dkv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float l2_lds[3][64];       // lse2 of the tile's queries (32 used)
   __shared__ __attribute__((aligned(16))) float dv_lds[3][64];       // Dvec of the tile's queries (32 used)
   __shared__ __attribute__((aligned(16))) int2 qw_lds[3][kT];        // {lo, hi} of the tile's queries
-  __shared__ __attribute__((aligned(16))) float4 p_lds[2][2][4 * 64];   // P from role A to role B, per pair
+  __shared__ __attribute__((aligned(16))) float4 p_lds[4][4 * 64];   // P from role A to role B, per pair
   __shared__ __attribute__((aligned(8))) uint8_t flags8[kKvMaxTiles];
   __shared__ uint16_t klist[kKvMaxTiles + kListPad];
   __shared__ int32_t krange[3][kKvWaves];
@@ -480,8 +519,8 @@ __global__ void __launch_bounds__(kKvThreads, 2) bwd_dkv_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool role_a = wave < 2;
-  const int pair = wave & 1;
+  const bool role_a = wave < 4;
+  const int pair = wave & 3;
   const int ql = lane & 31;   // key column owned by this lane
   const int hh = lane >> 5;
 
@@ -540,9 +579,9 @@ __global__ void __launch_bounds__(kKvThreads, 2) bwd_dkv_kernel(BwdArgs a) {
   const float c2 = a.scale * kLog2e;
   const int group = a.H / a.H_kv;
   const int n_qt = (a.Lq + kT - 1) / kT;
-  // this wave's share of a query tile: Q (waves 0, 1) or dO (waves 2, 3), LDS
+  // role B's share of an item's loads: Q (waves 4, 5) or dO (waves 6, 7), LDS
   // chunk slots ((wave & 1) * kLoads + i) * 64 + lane
-  const bool load_q = wave < 2;
+  const bool load_q = wave < 6;
   uint32_t ld_off[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i)
@@ -552,183 +591,242 @@ __global__ void __launch_bounds__(kKvThreads, 2) bwd_dkv_kernel(BwdArgs a) {
   TrFrags<D> trf;
   trf.init(lane);
 
-  for (int seg0 = 0; seg0 < n_qt && kmax >= 0; seg0 += kKvMaxTiles) {
-    const int nseg = min(kKvMaxTiles, n_qt - seg0);
-    // ---- classify the segment's query tiles: 8 lanes per tile, 4 queries each
-    bar();
-    for (int base = 0; base < nseg; base += kKvThreads / 8) {
-      const int tt = base + (tid >> 3);
-      const int g8 = tid & 7;
-      int lbmin = INT_MAX, lbmax = -1, ubmin = INT_MAX, ubmax = -1, dead = 0;
-      if (tt < nseg) {
-        const int q0 = (seg0 + tt) * kT + 4 * g8;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int j = q0 + e;
-          if (j < a.Lq) {
-            const int2 w = a.qwin[j];
-            if (w.x <= w.y) {
-              lbmin = min(lbmin, w.x);
-              lbmax = max(lbmax, w.x);
-              ubmin = min(ubmin, w.y);
-              ubmax = max(ubmax, w.y);
+  // The two roles run disjoint copies of the loop (a compile-time role), so
+  // the register allocator never has to hold one role's temporaries while
+  // the other's are live; both copies pass the same sequence of barriers.
+  auto run = [&](auto role) __attribute__((always_inline)) {
+    constexpr bool kA = decltype(role)::value;
+    for (int seg0 = 0; seg0 < n_qt && kmax >= 0; seg0 += kKvMaxTiles) {
+      const int nseg = min(kKvMaxTiles, n_qt - seg0);
+      // ---- classify the segment's query tiles: 8 lanes per tile, 4 queries each
+      bar();
+      for (int base = 0; base < nseg; base += kKvThreads / 8) {
+        const int tt = base + (tid >> 3);
+        const int g8 = tid & 7;
+        int lbmin = INT_MAX, lbmax = -1, ubmin = INT_MAX, ubmax = -1, dead = 0;
+        if (tt < nseg) {
+          const int q0 = (seg0 + tt) * kT + 4 * g8;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = q0 + e;
+            if (j < a.Lq) {
+              const int2 w = a.qwin[j];
+              if (w.x <= w.y) {
+                lbmin = min(lbmin, w.x);
+                lbmax = max(lbmax, w.x);
+                ubmin = min(ubmin, w.y);
+                ubmax = max(ubmax, w.y);
+              } else {
+                dead = 1;
+              }
             } else {
               dead = 1;
             }
-          } else {
-            dead = 1;
           }
         }
-      }
-#pragma unroll
-      for (int o = 4; o >= 1; o >>= 1) {
-        lbmin = min(lbmin, __shfl_xor(lbmin, o));
-        lbmax = max(lbmax, __shfl_xor(lbmax, o));
-        ubmin = min(ubmin, __shfl_xor(ubmin, o));
-        ubmax = max(ubmax, __shfl_xor(ubmax, o));
-        dead |= __shfl_xor(dead, o);
-      }
-      if (g8 == 0 && tt < nseg) {
-        // kept when some query of the tile may attend some key of the workgroup;
-        // full when every query may attend every key (and there are no pads)
-        const bool keep = ubmax >= 0 && kmax >= lbmin && kmin <= ubmax;
-        const bool full = !dead && !anypad && kmin >= lbmax && kmax <= ubmin;
-        flags8[tt] = (uint8_t)((keep ? 1 : 0) | ((keep && !full) ? 2 : 0));
-      }
-    }
-    bar();
-    const int nk = build_tile_list<kKvWaves, kListPad>(flags8, nseg, klist, wcount);
-    bar();
-    if (nk == 0) continue;
-    const int nitems = nk * group;   // (kept tile, query head of the group), head fastest
-
-    auto issue = [&](int item, int slot) __attribute__((always_inline)) {
-      const int u = item / group;
-      const int h = hk * group + (item - u * group);
-      const int j = klist[u] & 0x7fff;
-      const int q0 = (seg0 + j) * kT;
-      const uint32_t rows = (uint32_t)min(kT, a.Lq - q0);
-      const __bf16* base = load_q
-          ? static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)q0 * a.q_sl
-          : static_cast<const __bf16*>(a.dout) + b * a.do_sb + h * a.do_sh + (int64_t)q0 * a.do_sl;
-      const i32x4 rs = make_rsrc(base, rows * (uint32_t)(load_q ? a.q_sl : a.do_sl) * 2u);
-      __bf16* dst = load_q ? &q_lds[slot][0] : &g_lds[slot][0];
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) dma_b128(rs, ld_off[i], lds_addr(dst + ((wave & 1) * kLoads + i) * 512));
-      const int64_t qrow = (int64_t)(b * a.H + h) * a.Lq + q0;
-      if (wave == 0) {
-        dma_b32(make_rsrc(a.lse2 + qrow, rows * 4u), (uint32_t)lane * 4u, lds_addr(&l2_lds[slot][0]));
-      } else if (wave == 1) {
-        dma_b32(make_rsrc(a.dvec + qrow, rows * 4u), (uint32_t)lane * 4u, lds_addr(&dv_lds[slot][0]));
-      } else if (wave == 2) {
-        dma_b32(make_rsrc(a.qwin + q0, rows * 8u), (uint32_t)lane * 4u, lds_addr(&qw_lds[slot][0]));
-      }
-    };
-
-    // role A, item `it` in buffer `slot`
-    auto step_a = [&](int it, int slot) __attribute__((always_inline)) {
-      const int e = __builtin_amdgcn_readfirstlane((int)klist[it / group]);
-      const __bf16* qt_l = &q_lds[slot][0];
-      f32x16 sa = {};
-#pragma unroll
-      for (int kk = 0; kk < C::kKSteps; ++kk)
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowf.get(qt_l, kk), rf[kk], sa, 0, 0, 0);
-      // lane: key ql, queries 8 * i + 4 * hh + jj of the tile (element 4 * i + jj)
-      float p[16];
-      const int remq = a.Lq - (seg0 + (e & 0x7fff)) * kT - 4 * hh;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 l2 = *reinterpret_cast<const float4*>(&l2_lds[slot][8 * i + 4 * hh]);
-        const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
-        bool ok[4] = {true, true, true, true};
-        if (e & 0x8000) {
-          const int4 w0 = *reinterpret_cast<const int4*>(&qw_lds[slot][8 * i + 4 * hh]);
-          const int4 w1 = *reinterpret_cast<const int4*>(&qw_lds[slot][8 * i + 4 * hh + 2]);
-          const int lo[4] = {w0.x, w0.z, w1.x, w1.z};
-          const int hi[4] = {w0.y, w0.w, w1.y, w1.w};
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) ok[jj] = 8 * i + jj < remq && kp >= lo[jj] && kp <= hi[jj];
+  #pragma unroll
+        for (int o = 4; o >= 1; o >>= 1) {
+          lbmin = min(lbmin, __shfl_xor(lbmin, o));
+          lbmax = max(lbmax, __shfl_xor(lbmax, o));
+          ubmin = min(ubmin, __shfl_xor(ubmin, o));
+          ubmax = max(ubmax, __shfl_xor(ubmax, o));
+          dead |= __shfl_xor(dead, o);
         }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float e2 = __builtin_amdgcn_exp2f(fmaf(sa[4 * i + jj], c2, -l2v[jj]));
-          p[4 * i + jj] = ok[jj] ? e2 : 0.f;
+        if (g8 == 0 && tt < nseg) {
+          // kept when some query of the tile may attend some key of the workgroup;
+          // full when every query may attend every key (and there are no pads)
+          const bool keep = ubmax >= 0 && kmax >= lbmin && kmin <= ubmax;
+          const bool full = !dead && !anypad && kmin >= lbmax && kmax <= ubmin;
+          flags8[tt] = (uint8_t)((keep ? 1 : 0) | ((keep && !full) ? 2 : 0));
         }
-        p_lds[it & 1][pair][i * 64 + lane] = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
       }
-      const bf16x8 p0 = pack_chunk(p, 0), p1 = pack_chunk(p, 1);
-      const __bf16* gt_l = &g_lds[slot][0];
-#pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(gt_l, 0, dt), p0, acc[dt], 0, 0, 0);
-#pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(gt_l, 1, dt), p1, acc[dt], 0, 0, 0);
-    };
+      bar();
+      const int nk = build_tile_list<kKvWaves, kListPad>(flags8, nseg, klist, wcount);
+      bar();
+      if (nk == 0) continue;
+      const int nitems = nk * group;   // (kept tile, query head of the group), head fastest
 
-    // role B, item `it` in buffer `slot` (role A wrote its P one barrier earlier)
-    auto step_b = [&](int it, int slot) __attribute__((always_inline)) {
-      const __bf16* gt_l = &g_lds[slot][0];
-      f32x16 pa = {};
-#pragma unroll
-      for (int kk = 0; kk < C::kKSteps; ++kk)
-        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rowf.get(gt_l, kk), rf[kk], pa, 0, 0, 0);
-      float ds[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float4 dv = *reinterpret_cast<const float4*>(&dv_lds[slot][8 * i + 4 * hh]);
-        const float dvv[4] = {dv.x, dv.y, dv.z, dv.w};
-        const float4 pv = p_lds[it & 1][pair][i * 64 + lane];
-        const float pp[4] = {pv.x, pv.y, pv.z, pv.w};
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) ds[4 * i + jj] = pp[jj] * (pa[4 * i + jj] - dvv[jj]);
-      }
-      const bf16x8 d0 = pack_chunk(ds, 0), d1 = pack_chunk(ds, 1);
-      const __bf16* qt_l = &q_lds[slot][0];
-#pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(qt_l, 0, dt), d0, acc[dt], 0, 0, 0);
-#pragma unroll
-      for (int dt = 0; dt < C::kDTiles; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(trf.get(qt_l, 1, dt), d1, acc[dt], 0, 0, 0);
-    };
+      // role B's loads of item `item` into buffer item % 3
+      auto issue = [&](int item) __attribute__((always_inline)) {
+        const int slot = item % 3;
+        const int u = item / group;
+        const int h = hk * group + (item - u * group);
+        const int j = klist[u] & 0x7fff;
+        const int q0 = (seg0 + j) * kT;
+        const uint32_t rows = (uint32_t)min(kT, a.Lq - q0);
+        const __bf16* base = load_q
+            ? static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)q0 * a.q_sl
+            : static_cast<const __bf16*>(a.dout) + b * a.do_sb + h * a.do_sh + (int64_t)q0 * a.do_sl;
+        const i32x4 rs = make_rsrc(base, rows * (uint32_t)(load_q ? a.q_sl : a.do_sl) * 2u);
+        __bf16* dst = load_q ? &q_lds[slot][0] : &g_lds[slot][0];
+  #pragma unroll
+        for (int i = 0; i < kLoads; ++i) dma_b128(rs, ld_off[i], lds_addr(dst + ((wave & 1) * kLoads + i) * 512));
+        const int64_t qrow = (int64_t)(b * a.H + h) * a.Lq + q0;
+        if (wave == 4) {
+          dma_b32(make_rsrc(a.lse2 + qrow, rows * 4u), (uint32_t)lane * 4u, lds_addr(&l2_lds[slot][0]));
+        } else if (wave == 5) {
+          dma_b32(make_rsrc(a.dvec + qrow, rows * 4u), (uint32_t)lane * 4u, lds_addr(&dv_lds[slot][0]));
+        } else if (wave == 6) {
+          dma_b32(make_rsrc(a.qwin + q0, rows * 8u), (uint32_t)lane * 4u, lds_addr(&qw_lds[slot][0]));
+        }
+      };
 
-    issue(0, 0);
-    int slot = 0;   // buffer of item it; item it - 1 sits in (slot + 2) % 3
-    for (int it = 0; it <= nitems; ++it) {
+      // One wave plays one role, so the roles share their per-item state:
+      // sx holds S(k) (role A) or dP(k) (role B); bx0, bx1 the bf16 P of the
+      // previous item (B operand of dV) or its bf16 dS (B operand of dK).
+      f32x16 sx = {};
+      bf16x8 bx0 = {}, bx1 = {};
+
+      // role A on the matrix cores: S(k) when WS, then dV(k - 1) when WV
+      auto a_mfma = [&](int k, auto ws, auto wv) __attribute__((always_inline)) {
+        constexpr bool kS = decltype(ws)::value, kV = decltype(wv)::value;
+        constexpr int kNs = kS ? C::kKSteps : 0;
+        const __bf16* qt_l = &q_lds[k % 3][0];
+        const __bf16* gt_l = &g_lds[(k + 2) % 3][0];
+        mfma_stream<kNs + (kV ? 2 * C::kDTiles : 0), kV ? 2 : 1>(
+            [&](int m) {
+              if (m < kNs) return rowf.get(qt_l, m);
+              const int mm = m - kNs;
+              return trf.get(gt_l, mm / C::kDTiles, mm % C::kDTiles);
+            },
+            [&](int m, const bf16x8& f) {
+              if (m < kNs) {
+                sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, rf[m], m == 0 ? f32x16{} : sx, 0, 0, 0);
+              } else {
+                const int mm = m - kNs, dt = mm % C::kDTiles;
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, mm < C::kDTiles ? bx0 : bx1, acc[dt], 0, 0, 0);
+              }
+            });
+      };
+
+      // role A: P(k) = 2^(S(k) c - lse2(k)), masked; to LDS for role B, bf16 kept for dV(k)
+      auto a_valu = [&](int k) __attribute__((always_inline)) {
+        const int slot = k % 3;
+        const int e = __builtin_amdgcn_readfirstlane((int)klist[k / group]);
+        // lane: key ql, queries 8 * i + 4 * hh + jj of the tile (element 4 * i + jj)
+        float p[16];
+        const int remq = a.Lq - (seg0 + (e & 0x7fff)) * kT - 4 * hh;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 l2 = *reinterpret_cast<const float4*>(&l2_lds[slot][8 * i + 4 * hh]);
+          const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
+          bool ok[4] = {true, true, true, true};
+          if (e & 0x8000) {
+            const int4 w0 = *reinterpret_cast<const int4*>(&qw_lds[slot][8 * i + 4 * hh]);
+            const int4 w1 = *reinterpret_cast<const int4*>(&qw_lds[slot][8 * i + 4 * hh + 2]);
+            const int lo[4] = {w0.x, w0.z, w1.x, w1.z};
+            const int hi[4] = {w0.y, w0.w, w1.y, w1.w};
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj) ok[jj] = 8 * i + jj < remq && kp >= lo[jj] && kp <= hi[jj];
+          }
+  #pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const float e2 = __builtin_amdgcn_exp2f(fmaf(sx[4 * i + jj], c2, -l2v[jj]));
+            p[4 * i + jj] = ok[jj] ? e2 : 0.f;
+          }
+          p_lds[pair][i * 64 + lane] = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+        }
+        bx0 = pack_chunk(p, 0);
+        bx1 = pack_chunk(p, 1);
+      };
+
+      // role B on the matrix cores: dP(k) when WP, then dK(k - 1) when WK
+      auto b_mfma = [&](int k, auto wp, auto wk) __attribute__((always_inline)) {
+        constexpr bool kP = decltype(wp)::value, kK = decltype(wk)::value;
+        constexpr int kNp = kP ? C::kKSteps : 0;
+        const __bf16* gt_l = &g_lds[k % 3][0];
+        const __bf16* qt_l = &q_lds[(k + 2) % 3][0];
+        mfma_stream<kNp + (kK ? 2 * C::kDTiles : 0), kK ? 2 : 1>(
+            [&](int m) {
+              if (m < kNp) return rowf.get(gt_l, m);
+              const int mm = m - kNp;
+              return trf.get(qt_l, mm / C::kDTiles, mm % C::kDTiles);
+            },
+            [&](int m, const bf16x8& f) {
+              if (m < kNp) {
+                sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, rf[m], m == 0 ? f32x16{} : sx, 0, 0, 0);
+              } else {
+                const int mm = m - kNp, dt = mm % C::kDTiles;
+                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, mm < C::kDTiles ? bx0 : bx1, acc[dt], 0, 0, 0);
+              }
+            });
+      };
+
+      // role B: dS(k) = P(k) * (dP(k) - Dvec(k))
+      auto b_valu = [&](int k) __attribute__((always_inline)) {
+        const int slot = k % 3;
+        float ds[16];
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 dv = *reinterpret_cast<const float4*>(&dv_lds[slot][8 * i + 4 * hh]);
+          const float dvv[4] = {dv.x, dv.y, dv.z, dv.w};
+          const float4 pv = p_lds[pair][i * 64 + lane];
+          const float pp[4] = {pv.x, pv.y, pv.z, pv.w};
+  #pragma unroll
+          for (int jj = 0; jj < 4; ++jj) ds[4 * i + jj] = pp[jj] * (sx[4 * i + jj] - dvv[jj]);
+        }
+        bx0 = pack_chunk(ds, 0);
+        bx1 = pack_chunk(ds, 1);
+      };
+
+      // one pair of phases (see above) for item k; the first (k = 0) and the
+      // last (k = nitems) have no previous or no current item
+      auto phases = [&](int k, auto first, auto last) __attribute__((always_inline)) {
+        constexpr bool kFirst = decltype(first)::value, kLast = decltype(last)::value;
+        // phase 2k: A on the matrix cores, B on the vector ALU (+ loads of item k + 1)
+        if (kA) {
+          a_mfma(k, std::integral_constant<bool, !kLast>{}, std::integral_constant<bool, !kFirst>{});
+        } else {
+          if (!kLast && k + 1 < nitems) issue(k + 1);
+          if (!kFirst) b_valu(k - 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        bar();
+        // phase 2k+1: A on the vector ALU, B on the matrix cores
+        if (kA) {
+          if (!kLast) a_valu(k);
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          b_mfma(k, std::integral_constant<bool, !kLast>{}, std::integral_constant<bool, !kFirst>{});
+          __builtin_amdgcn_sched_barrier(0);
+          vm_wait<0>();   // the loads of item k + 1 have landed
+        }
+        bar();
+      };
+
+      // prologue: item 0 in LDS
+      if (!kA) issue(0);
       vm_wait<0>();
-      bar();   // item it is in LDS, P of item it - 1 is written, buffer (it + 1) % 3 is free
-      const int nslot = slot == 2 ? 0 : slot + 1;
-      if (it + 1 < nitems) issue(it + 1, nslot);
-      if (role_a) {
-        if (it < nitems) step_a(it, slot);
-      } else if (it >= 1) {
-        step_b(it - 1, slot == 0 ? 2 : slot - 1);
-      }
-      slot = nslot;
+      bar();
+      phases(0, std::true_type{}, std::false_type{});
+      for (int k = 1; k < nitems; ++k) phases(k, std::false_type{}, std::false_type{});
+      phases(nitems, std::false_type{}, std::true_type{});
     }
-  }
 
-  if (!k_in) return;
-  const int64_t krow = (int64_t)bhk * lk_total + k_idx;
-  float* out = (role_a ? a.dv : a.dk) + krow * D;
-  const float sc = role_a ? 1.f : a.scale;
-#pragma unroll
-  for (int dt = 0; dt < C::kDTiles; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float4 x = make_float4(sc * acc[dt][4 * i + 0], sc * acc[dt][4 * i + 1], sc * acc[dt][4 * i + 2],
-                             sc * acc[dt][4 * i + 3]);
-      float4* p = reinterpret_cast<float4*>(out + 32 * dt + 8 * i + 4 * hh);
-      if (a.accumulate) {
-        const float4 y = *p;
-        x.x += y.x;
-        x.y += y.y;
-        x.z += y.z;
-        x.w += y.w;
+    if (!k_in) return;
+    const int64_t krow = (int64_t)bhk * lk_total + k_idx;
+    float* out = (kA ? a.dv : a.dk) + krow * D;
+    const float sc = kA ? 1.f : a.scale;
+  #pragma unroll
+    for (int dt = 0; dt < C::kDTiles; ++dt)
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4 x = make_float4(sc * acc[dt][4 * i + 0], sc * acc[dt][4 * i + 1], sc * acc[dt][4 * i + 2],
+                               sc * acc[dt][4 * i + 3]);
+        float4* p = reinterpret_cast<float4*>(out + 32 * dt + 8 * i + 4 * hh);
+        if (a.accumulate) {
+          const float4 y = *p;
+          x.x += y.x;
+          x.y += y.y;
+          x.z += y.z;
+          x.w += y.w;
+        }
+        *p = x;
       }
-      *p = x;
-    }
+
+  };
+  if (role_a) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 template <int D>
