@@ -150,9 +150,11 @@ cpr_status cp_ring_attn_init(int32_t B, int32_t H, int32_t Lq, int32_t D, float*
                     "cp_ring_attn_init");
 }
 
+// need_q_pos = 0 for calls that take no query positions (the backward step,
+// whose windows come with the prepared workspace)
 static cpr_status validate_attn(int32_t dtype, int32_t B, int32_t H, int32_t D, const cpr_view* q, int32_t Lq,
                                 const int32_t* q_pos, const cpr_view* k, const cpr_view* v, int64_t Lk_total,
-                                const int32_t* kv_pos, const cpr_attn_ext* ext) {
+                                const int32_t* kv_pos, const cpr_attn_ext* ext, int need_q_pos = 1) {
   TRY(check_dims(dtype, B, H, D));
   if (ext) {
     if (ext->H_kv < 0 || (ext->H_kv > 0 && H % ext->H_kv != 0))
@@ -165,7 +167,7 @@ static cpr_status validate_attn(int32_t dtype, int32_t B, int32_t H, int32_t D, 
   TRY(check_view("q", q, dtype));
   TRY(check_view("k", k, dtype));
   TRY(check_view("v", v, dtype));
-  if (!q_pos || !kv_pos) return fail(CPR_EINVAL, "position arrays must be non-NULL");
+  if ((need_q_pos && !q_pos) || !kv_pos) return fail(CPR_EINVAL, "position arrays must be non-NULL");
   TRY(check_grid(B, H, Lq));
   TRY(check_grid(B, ext && ext->H_kv > 0 ? ext->H_kv : H, (int32_t)Lk_total));   // Lk_total <= 2^30 here
   return CPR_OK;
@@ -399,10 +401,8 @@ cpr_status cp_ring_attn_bwd_step(int32_t dtype, int32_t B, int32_t H, int32_t D,
                                  const cpr_view* k, const cpr_view* v, int32_t Lk, const int32_t* kv_pos,
                                  float softmax_scale, const void* workspace, size_t workspace_bytes,
                                  float* dq_acc, float* dk_acc, float* dv_acc, void* stream) {
-  // the step takes no query positions (the windows come with the workspace):
-  // kv_pos stands in for the non-NULL check of q_pos
   cpr_attn_ext ext{H_kv, nullptr, nullptr};
-  TRY(validate_attn(dtype, B, H, D, q, Lq, kv_pos, k, v, Lk, kv_pos, &ext));
+  TRY(validate_attn(dtype, B, H, D, q, Lq, nullptr, k, v, Lk, kv_pos, &ext, /*need_q_pos=*/0));
   TRY(check_view("dout", dout, dtype));
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(CPR_EINVAL, "softmax_scale must be finite");

@@ -271,3 +271,13 @@ def test_bwd_full_size_sampled(wl_name):
     got_v = dv[0, h0, torch.from_numpy(k_rows).cuda()].cpu().numpy()
     for g, r, n in ((got_q, ref_q, "dQ"), (got_k, ref_k, "dK"), (got_v, ref_v, "dV")):
         check(g, r, "bf16", f"{wl_name} head {h0} sampled {n}")
+
+
+def test_bwd_is_deterministic():
+    """No atomics: the same inputs give bit-identical gradients."""
+    c = Case("bf16", 1, 4, 2, 128, 1500, 2, "zigzag", True, seed=309)
+    ri, do_local, o_dev, lse_dev, kw, _ = c.rank(0)
+    a = c.run_gpu(0, ri, do_local, o_dev, lse_dev, kw)
+    b = c.run_gpu(0, ri, do_local, o_dev, lse_dev, kw)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)

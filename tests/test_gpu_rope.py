@@ -109,3 +109,12 @@ def test_rope_in_place_and_strided_input():
     torch.cuda.synchronize()
     assert torch.equal(y, want)
     assert torch.equal(sub, want[:, ::2])
+
+
+def test_rope_is_deterministic():
+    x = torch.randn((2, 4, 777, 128), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).cuda()
+    pos = torch.arange(100, 877, dtype=torch.int32, device="cuda")
+    a = cpr.cp_rope_apply(x, pos, style=cpr.ROPE_HALF)
+    b = cpr.cp_rope_apply(x, pos, style=cpr.ROPE_HALF)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
