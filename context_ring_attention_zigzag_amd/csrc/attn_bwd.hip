@@ -169,6 +169,20 @@ __device__ __forceinline__ void mfma_stream(Fetch&& fetch, Mma&& mma) {
   }
 }
 
+// mfma_stream with side(m) called after MFMA m (e.g. to issue loads between MFMAs)
+template <int N, int kReads, typename Fetch, typename Mma, typename Side>
+__device__ __forceinline__ void mfma_stream_side(Fetch&& fetch, Mma&& mma, Side&& side) {
+  bf16x8 fr[kPf + 1];
+#pragma unroll
+  for (int m = 0; m < kPf && m < N; ++m) fr[m] = fetch(m);
+#pragma unroll
+  for (int m = 0; m < N; ++m) {
+    if (m + kPf < N) fr[(m + kPf) % (kPf + 1)] = fetch(m + kPf);
+    mma(m, fr[m % (kPf + 1)]);
+    side(m);
+  }
+}
+
 // workgroup index -> logical index with the workgroups of one head on one XCD
 __device__ __forceinline__ int xcd_logical(int w, int ntiles) {
   const int xcd = w % kXcds, idx = w / kXcds;
@@ -485,14 +499,14 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
 // resident, dK accumulated) own the same keys and share SIMD s. Query tiles
 // (items) run in phases separated by workgroup barriers, and in every phase one
 // role works the matrix cores while the other works the vector ALU:
-//   phase 2k:   A: S(k) = Q(k) K^T, then dV^T += dO(k-1)^T P(k-1)   [MFMA]
-//               B: dS(k-1) = P(k-1) * (dP(k-1) - Dvec(k-1)), and the
-//                  loads of item k + 1                               [VALU]
+//   phase 2k:   A: S(k) = Q(k) K^T, then dV^T += dO(k-1)^T P(k-1),
+//                  with the loads of item k + 1 between the MFMAs    [MFMA]
+//               B: dS(k-1) = P(k-1) * (dP(k-1) - Dvec(k-1))          [VALU]
 //   phase 2k+1: A: P(k) = 2^(S(k) c - lse2(k)), masked, handed to B
 //                  through LDS in float32                            [VALU]
 //               B: dP(k) = dO(k) V^T, then dK^T += Q(k-1)^T dS(k-1)  [MFMA]
 // Items rotate through three LDS buffers: phase 2k reads items k - 1 and k,
-// loads item k + 1 into the buffer of item k - 2, and role B waits for those
+// loads item k + 1 into the buffer of item k - 2, and role A waits for those
 // loads at the end of phase 2k + 1, one barrier before their first reader.
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
@@ -502,7 +516,7 @@ constexpr int kKvMaxTiles = 8 * kKvThreads;   // query tiles classified per segm
 template <int D>
 __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
   using C = BCfg<D>;
-  constexpr int kLoads = C::kTileLoads / 2;   // per role-B wave: two waves per tensor
+  constexpr int kLoads = C::kTileLoads / 2;   // per role-A wave: two waves per tensor
   static_assert(kLoads >= 1 && C::kTileLoads % 2 == 0, "tile/waves mismatch");
 
   __shared__ __attribute__((aligned(16))) __bf16 q_lds[3][kT * D];   // Q tiles (S A operand, Q^T reads)
@@ -579,9 +593,9 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
   const float c2 = a.scale * kLog2e;
   const int group = a.H / a.H_kv;
   const int n_qt = (a.Lq + kT - 1) / kT;
-  // role B's share of an item's loads: Q (waves 4, 5) or dO (waves 6, 7), LDS
+  // role A's share of an item's loads: Q (waves 0, 1) or dO (waves 2, 3), LDS
   // chunk slots ((wave & 1) * kLoads + i) * 64 + lane
-  const bool load_q = wave < 6;
+  const bool load_q = wave < 2;
   uint32_t ld_off[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i)
@@ -646,8 +660,15 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       if (nk == 0) continue;
       const int nitems = nk * group;   // (kept tile, query head of the group), head fastest
 
-      // role B's loads of item `item` into buffer item % 3
-      auto issue = [&](int item) __attribute__((always_inline)) {
+      // role A's loads of item `item` into buffer item % 3, one at a time
+      // (load n = 0 .. kLoads of this wave), so that they can go out between
+      // the MFMAs of its matrix phase
+      struct Plan {
+        i32x4 rs, rx;
+        uint32_t dst, dx;
+      };
+      auto plan = [&](int item) __attribute__((always_inline)) -> Plan {
+        Plan pl;
         const int slot = item % 3;
         const int u = item / group;
         const int h = hk * group + (item - u * group);
@@ -657,18 +678,24 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
         const __bf16* base = load_q
             ? static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)q0 * a.q_sl
             : static_cast<const __bf16*>(a.dout) + b * a.do_sb + h * a.do_sh + (int64_t)q0 * a.do_sl;
-        const i32x4 rs = make_rsrc(base, rows * (uint32_t)(load_q ? a.q_sl : a.do_sl) * 2u);
-        __bf16* dst = load_q ? &q_lds[slot][0] : &g_lds[slot][0];
-  #pragma unroll
-        for (int i = 0; i < kLoads; ++i) dma_b128(rs, ld_off[i], lds_addr(dst + ((wave & 1) * kLoads + i) * 512));
+        pl.rs = make_rsrc(base, rows * (uint32_t)(load_q ? a.q_sl : a.do_sl) * 2u);
+        pl.dst = lds_addr(load_q ? &q_lds[slot][0] : &g_lds[slot][0]) + (uint32_t)((wave & 1) * kLoads) * 1024u;
         const int64_t qrow = (int64_t)(b * a.H + h) * a.Lq + q0;
-        if (wave == 4) {
-          dma_b32(make_rsrc(a.lse2 + qrow, rows * 4u), (uint32_t)lane * 4u, lds_addr(&l2_lds[slot][0]));
-        } else if (wave == 5) {
-          dma_b32(make_rsrc(a.dvec + qrow, rows * 4u), (uint32_t)lane * 4u, lds_addr(&dv_lds[slot][0]));
-        } else if (wave == 6) {
-          dma_b32(make_rsrc(a.qwin + q0, rows * 8u), (uint32_t)lane * 4u, lds_addr(&qw_lds[slot][0]));
+        if (wave == 0) {
+          pl.rx = make_rsrc(a.lse2 + qrow, rows * 4u);
+          pl.dx = lds_addr(&l2_lds[slot][0]);
+        } else if (wave == 1) {
+          pl.rx = make_rsrc(a.dvec + qrow, rows * 4u);
+          pl.dx = lds_addr(&dv_lds[slot][0]);
+        } else {
+          pl.rx = make_rsrc(a.qwin + q0, rows * 8u);
+          pl.dx = lds_addr(&qw_lds[slot][0]);
         }
+        return pl;
+      };
+      auto load_n = [&](const Plan& pl, int n) __attribute__((always_inline)) {
+        if (n < kLoads) dma_b128(pl.rs, ld_off[n], pl.dst + (uint32_t)n * 1024u);
+        else if (wave < 3) dma_b32(pl.rx, (uint32_t)lane * 4u, pl.dx);
       };
 
       // One wave plays one role, so the roles share their per-item state:
@@ -681,9 +708,14 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       auto a_mfma = [&](int k, auto ws, auto wv) __attribute__((always_inline)) {
         constexpr bool kS = decltype(ws)::value, kV = decltype(wv)::value;
         constexpr int kNs = kS ? C::kKSteps : 0;
+        constexpr int kN = kNs + (kV ? 2 * C::kDTiles : 0);
         const __bf16* qt_l = &q_lds[k % 3][0];
         const __bf16* gt_l = &g_lds[(k + 2) % 3][0];
-        mfma_stream<kNs + (kV ? 2 * C::kDTiles : 0), kV ? 2 : 1>(
+        const bool more = k + 1 < nitems;
+        const Plan pl = plan(more ? k + 1 : k);
+        // load n of item k + 1 goes out after MFMA 1 + 3n: the address unit
+        // drains while the matrix cores work instead of stalling a vector phase
+        mfma_stream_side<kN, kV ? 2 : 1>(
             [&](int m) {
               if (m < kNs) return rowf.get(qt_l, m);
               const int mm = m - kNs;
@@ -696,7 +728,16 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
                 const int mm = m - kNs, dt = mm % C::kDTiles;
                 acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, mm < C::kDTiles ? bx0 : bx1, acc[dt], 0, 0, 0);
               }
+            },
+            [&](int m) {
+              if (more && m % 3 == 1 && m / 3 <= kLoads) load_n(pl, m / 3);
             });
+        // the loads a short stream had no room for
+        if (more) {
+#pragma unroll
+          for (int n = 0; n <= kLoads; ++n)
+            if (3 * n + 1 >= kN) load_n(pl, n);
+        }
       };
 
       // role A: P(k) = 2^(S(k) c - lse2(k)), masked; to LDS for role B, bf16 kept for dV(k)
@@ -777,7 +818,6 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
         if (kA) {
           a_mfma(k, std::integral_constant<bool, !kLast>{}, std::integral_constant<bool, !kFirst>{});
         } else {
-          if (!kLast && k + 1 < nitems) issue(k + 1);
           if (!kFirst) b_valu(k - 1);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -786,16 +826,20 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
         if (kA) {
           if (!kLast) a_valu(k);
           __builtin_amdgcn_sched_barrier(0);
+          vm_wait<0>();   // the loads of item k + 1 have landed
         } else {
           b_mfma(k, std::integral_constant<bool, !kLast>{}, std::integral_constant<bool, !kFirst>{});
           __builtin_amdgcn_sched_barrier(0);
-          vm_wait<0>();   // the loads of item k + 1 have landed
         }
         bar();
       };
 
       // prologue: item 0 in LDS
-      if (!kA) issue(0);
+      if (kA) {
+        const Plan p0 = plan(0);
+#pragma unroll
+        for (int n = 0; n <= kLoads; ++n) load_n(p0, n);
+      }
       vm_wait<0>();
       bar();
       phases(0, std::true_type{}, std::false_type{});
