@@ -15,15 +15,16 @@
 //  * two wave groups (waves [0, NW/2) and [NW/2, NW), one wave of each per
 //    SIMD) run the same key-tile sequence one phase apart. Each tile takes two
 //    phases: an MFMA phase (S^T = K Q^T of this tile, then P*V of the previous
-//    one, with the row max of the new scores beside it) and a VALU phase
-//    (mask, rescale decision, exponentials, row sums, tile loads). While one
+//    one, with the row max of the new scores and the tile loads beside it) and
+//    a VALU phase (mask, rescale decision, exponentials, row sums). While one
 //    group is in its MFMA phase the other is in its VALU phase, so the matrix
 //    cores and the vector ALUs of every SIMD work at the same time; a
 //    workgroup barrier separates consecutive phases;
 //  * keys stream through LDS in tiles of BN = 64 with direct buffer->LDS
-//    16-byte loads, into three K and three V buffers; every wave waits for its
-//    own loads one tile after issuing them, one barrier before their first
-//    reader;
+//    16-byte loads, into three K and three V buffers, issued from the middle of
+//    the MFMA phase (the vector phase is the longer one); every wave waits for
+//    its own loads at the end of its next MFMA phase, one barrier before their
+//    first reader;
 //  * scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_bf16: lane l then holds query l%32 and 16 of the 32
 //    keys of a 32x32 block, so the per-query max and sum are lane-local plus
@@ -66,6 +67,7 @@ constexpr int kListPad = 8;     // end markers after the last kept tile (look-ah
 #define CPR_M_PREFETCH 5
 #endif
 constexpr int kMPrefetch = CPR_M_PREFETCH;   // MFMAs whose LDS operand reads are in flight
+constexpr int kKLoadAt = 8;                  // MFMA of the MFMA phase before which the K loads go out
 
 template <int D, int NW>
 struct Cfg {
@@ -335,12 +337,6 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         const int r0 = j < nseg ? (seg0 + j) * kBN : 0;
         dma_b32(make_rsrc(posb + r0, tile_rows(j) * 4u), ldp, lds_addr(&pos_lds[slot][0]));
       };
-      // load number n of a VALU phase: K chunks first, then V chunks
-      auto load_nth = [&](auto n, int jk, int jv, __bf16* kd, __bf16* vd) __attribute__((always_inline)) {
-        constexpr int N = decltype(n)::value;
-        if constexpr (N < C::kLoadsPerWave) load_k(jk, ic<N>{}, kd);
-        else load_v(jv, ic<N - C::kLoadsPerWave>{}, vd);
-      };
       auto load_tile_k = [&](int j, __bf16* dst) __attribute__((always_inline)) {
         if constexpr (C::kLoadsPerWave >= 1) load_k(j, ic<0>{}, dst);
         if constexpr (C::kLoadsPerWave >= 2) load_k(j, ic<1>{}, dst);
@@ -356,8 +352,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       // (kNB MFMAs). Every MFMA's A operand is a 4-register fragment read from LDS
       // kMPrefetch MFMAs ahead through one ring, across the switch from K to V.
       // The read / MFMA order is pinned with scheduling-group barriers.
-      auto mphase = [&](auto kslot, auto vslot, auto with_pv, f32x16 (&s)[2], const bf16x8 (&pb)[4])
-          __attribute__((always_inline)) {
+      // hook(m) runs before MFMA m of the stream and, with m = kN, after the last
+      auto mphase = [&](auto kslot, auto vslot, auto with_pv, f32x16 (&s)[2], const bf16x8 (&pb)[4],
+                        auto&& hook) __attribute__((always_inline)) {
         constexpr int kNA = 2 * C::kKSteps;
         constexpr int kN = kNA + (decltype(with_pv)::value ? C::kNB : 0);
         constexpr int kPf = kMPrefetch;
@@ -382,6 +379,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int m = 0; m < kN; ++m) {
           if (m + kPf < kN) fetch(m + kPf);
+          hook(m);
           if (m < kNA) {
             const int kk = m >> 1, kt = m & 1;
             if (kk == 0) {
@@ -396,6 +394,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
             ot[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr[m % (kPf + 1)], pb[ch], ot[dt], 0, 0, 0);
           }
         }
+        hook(kN);
         // pinned order: the first kPf fetches, then per MFMA: its look-ahead fetch, the MFMA
 #pragma unroll
         for (int m = 0; m < kPf; ++m) {
@@ -483,22 +482,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       // Empty asm statements that read the given registers: the values must be
       // computed before this point in program order, which keeps the MFMAs of
       // an MFMA phase and the exponentials of a VALU phase from drifting across
-      // the phase barrier, and spaces the loads between the exponentials.
+      // the phase barrier.
       // (Vector-register constraints exist only in the device pass.)
       auto pin_scores = [&](const f32x16 (&x)[2], const float& m) __attribute__((always_inline)) {
 #if defined(__HIP_DEVICE_COMPILE__)
         asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(m));
-#endif
-      };
-      auto pin_chunk = [&](const bf16x8& x) __attribute__((always_inline)) {
-#if defined(__HIP_DEVICE_COMPILE__)
-        asm volatile("" ::"v"(x));
-#endif
-      };
-      // (an empty asm statement that may change x: what uses x afterwards stays after it)
-      auto after_here = [&](float& x) __attribute__((always_inline)) {
-#if defined(__HIP_DEVICE_COMPILE__)
-        asm volatile("" : "+v"(x));
 #endif
       };
       auto pin_probs = [&](const bf16x8 (&x)[4]) __attribute__((always_inline)) {
@@ -510,13 +498,15 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       // Kept tiles 0, 1, ... of the list in order; tile u uses K buffer u%3, V
       // buffer u%3 and position buffer u%4. Global phases: group 0 runs the MFMA
       // phase of tile u in phase 2u and its VALU phase in 2u+1; group 1 runs them
-      // in 2u+1 and 2u+2. In its VALU phase of tile u a wave of group 0 loads its
-      // share of K of tile u+2 and V of tile u+1, a wave of group 1 its share of K
-      // of tile u+3 and V of tile u+2 (wave NW-1 also the positions of tile u+3):
-      // each buffer is free by then (its last readers ran before the preceding
-      // barrier), and each wave waits for its loads at the end of its next VALU
-      // phase, one barrier before the first reader of the data. The list entries
-      // of tiles u .. u+3 ride in e0 .. e3.
+      // in 2u+1 and 2u+2. The MFMA phase of tile u reads K of tile u and V of
+      // tile u-1, and loads this wave's share of K of tile u+2 (after the eighth
+      // MFMA) and V of tile u+1 (between the score and the P*V MFMAs): those
+      // buffers held K of tile u-1 and V of tile u-2, whose last readers (group
+      // 1's MFMA phase of tile u-1) ran before the preceding barrier. Each wave
+      // waits for these loads at the end of its next MFMA phase, one barrier
+      // before the MFMA phase of tile u+2 reads them. The VALU phase of tile u
+      // loads (wave NW-1) the positions of tile u+3. The list entries of tiles
+      // u .. u+3 ride in e0 .. e3.
       int u = 0;
       int e0 = __builtin_amdgcn_readfirstlane((int)klist[0]);
       int e1 = __builtin_amdgcn_readfirstlane((int)klist[1]);
@@ -527,48 +517,20 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       f32x16 s[2];
       bf16x8 pb[4];
 
-      auto vphase = [&](auto kslot, bool has, float mxh) __attribute__((always_inline)) {
-        constexpr int KS = decltype(kslot)::value;   // u % 3
-        constexpr int kL = C::kLoadsPerWave;
+      auto vphase = [&](bool has, float mxh) __attribute__((always_inline)) {
         const int ahead = klist[u + 4];              // read now, used at the end
-        __bf16* kd = group == 0 ? kbuf(ic<(KS + 2) % 3>{}) : kbuf(ic<KS>{});
-        __bf16* vd = group == 0 ? vbuf(ic<(KS + 1) % 3>{}) : vbuf(ic<(KS + 2) % 3>{});
-        const int jk = tix(group == 0 ? e2 : e3);
-        const int jv = tix(group == 0 ? e1 : e2);
         if (has) {
-          // load n goes out between exponential chunks n-1 and n (pinned in
-          // program order), so the loads of the four waves of a group reach the
-          // memory pipeline spread over the phase instead of queueing at its start
           float mu;
-          load_nth(ic<0>{}, jk, jv, kd, vd);
           softmax_max(s, e0, u & 3, mxh);
           mu = m_use;
           softmax_exp(s, pb, ic<0>{}, mu);
-          pin_chunk(pb[0]);
-          load_nth(ic<1>{}, jk, jv, kd, vd);
-          after_here(mu);
           softmax_exp(s, pb, ic<1>{}, mu);
-          if constexpr (2 * kL > 2) {
-            pin_chunk(pb[1]);
-            load_nth(ic<2>{}, jk, jv, kd, vd);
-            after_here(mu);
-          }
           softmax_exp(s, pb, ic<2>{}, mu);
-          if constexpr (2 * kL > 3) {
-            pin_chunk(pb[2]);
-            load_nth(ic<3>{}, jk, jv, kd, vd);
-            after_here(mu);
-          }
           softmax_exp(s, pb, ic<3>{}, mu);
-        } else {
-          load_tile_k(jk, kd);
-          load_tile_v(jv, vd);
         }
+        // (lands by the end of this wave's next MFMA phase, with the tile loads)
         if (wave == NW - 1) load_pos(tix(e3), (u + 3) & 3);
         pin_probs(pb);
-        // the loads of the previous VALU phase have landed
-        if (wave == NW - 1) vm_wait<2 * kL + 1>();
-        else vm_wait<2 * kL>();
         e0 = e1;
         e1 = e2;
         e2 = e3;
@@ -577,16 +539,20 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         bar();
       };
 
-      // prologue: K of tiles 0 and 1, V of tile 0, positions of tiles 0 .. 2;
-      // group 1, which loads one tile further ahead, also its share of K of tile 2
-      // and V of tile 1
+      // the MFMA phase's loads of tile u: K of tile u+2 after MFMA kKLoadAt, V of
+      // tile u+1 at the switch from the scores to P*V (or at the end of a stream
+      // without P*V)
+      auto mloads = [&](auto kslot, int m, int n_mfma) __attribute__((always_inline)) {
+        constexpr int KS = decltype(kslot)::value;
+        constexpr int kNA = 2 * C::kKSteps;
+        if (m == min(kKLoadAt, n_mfma)) load_tile_k(tix(e2), kbuf(ic<(KS + 2) % 3>{}));
+        if (m == min(kNA, n_mfma)) load_tile_v(tix(e1), vbuf(ic<(KS + 1) % 3>{}));
+      };
+
+      // prologue: K of tiles 0 and 1, V of tile 0, positions of tiles 0 .. 2
       load_tile_k(tix(e0), k_lds0);
       load_tile_k(tix(e1), k_lds1);
       load_tile_v(tix(e0), v_lds0);
-      if (group == 1) {
-        load_tile_k(tix(e2), k_lds2);
-        load_tile_v(tix(e1), v_lds1);
-      }
       if (wave == NW - 1) {
         load_pos(tix(e0), 0);
         load_pos(tix(e1), 1);
@@ -597,11 +563,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       if (group == 1) bar();   // group 1 trails by one phase
 
       // tile 0: no P*V yet
-      mphase(ic<0>{}, ic<2>{}, ic<0>{}, s, pb);
+      mphase(ic<0>{}, ic<2>{}, ic<0>{}, s, pb, [&](int m) { mloads(ic<0>{}, m, 2 * C::kKSteps); });
       float mxh = row_max(s);
       pin_scores(s, mxh);
+      vm_wait<2 * C::kLoadsPerWave>();
       bar();
-      vphase(ic<0>{}, true, mxh);
+      vphase(true, mxh);
 
       // tile u >= 1; after the last kept tile one more MFMA phase finishes P*V
       auto tile = [&](auto kslot) __attribute__((always_inline)) -> bool {
@@ -610,12 +577,16 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         // scores of this tile first (the VALU phase needs them), then P*V of the
         // previous tile; its last MFMAs may still run when the barrier passes,
         // since only the LDS reads have to be complete there
-        mphase(ic<KS>{}, ic<(KS + 2) % 3>{}, ic<1>{}, s, pb);   // stale K when !has: scores never used
+        // (stale K when !has: the scores are never used)
+        mphase(ic<KS>{}, ic<(KS + 2) % 3>{}, ic<1>{}, s, pb,
+               [&](int m) { mloads(kslot, m, 2 * C::kKSteps + C::kNB); });
         // the row max of the new scores, beside the P*V MFMAs of this phase
         mxh = row_max(s);
         pin_scores(s, mxh);
+        // this wave's tile loads of the previous MFMA phase have landed
+        vm_wait<2 * C::kLoadsPerWave>();
         bar();
-        vphase(kslot, has, mxh);
+        vphase(has, mxh);
         return has;
       };
       while (true) {
