@@ -30,15 +30,15 @@
 //    leave the accumulators already in the B-operand layout of
 //    dQ^T += K^T dS^T (v_cvt_pk_bf16_f32, round to nearest even); two
 //    workgroups share a CU;
-//  * the dK/dV kernel: a workgroup owns 64 keys of one (b, kv head) as two
+//  * the dK/dV kernel: a workgroup owns 128 keys of one (b, kv head) as four
 //    pairs of waves, 32 keys per pair, and streams query tiles (Q, dO, lse2,
 //    Dvec, windows) of every query head of the grouped-query group through
-//    three LDS buffers. The two waves of a pair split the work of each tile:
-//    role A computes S = Q K^T and P (masked) and dV^T += dO^T P with K
-//    resident; role B, one tile behind, computes dP = dO V^T and dS = P * (dP -
-//    Dvec) with P handed over through LDS in float32, and dK^T += Q^T dS with V
-//    resident. Each wave then holds half the resident operands and
-//    accumulators, and two workgroups share a CU;
+//    three LDS buffers. The two waves of a pair share a SIMD and split the work
+//    of each tile: role A computes S = Q K^T and P (masked) and dV^T += dO^T P
+//    with K resident; role B computes dP = dO V^T and dS = P * (dP - Dvec) with
+//    P handed over through LDS in float32, and dK^T += Q^T dS with V resident.
+//    The roles alternate between matrix and vector work phase by phase, so one
+//    wave's MFMAs run beside the other's exponentials or dS products;
 //  * both kernels classify the streamed tiles against the rows they own from
 //    position ranges (skip / full / masked) and walk an ordered list of the
 //    kept ones, as the forward kernel does; the grid keeps the workgroups of
