@@ -322,11 +322,12 @@ def main():
     del nat
     o = torch.empty_like(ri.q_local)
     lse = torch.empty(ri.q_local.shape[:3], dtype=torch.float32, device="cuda")
-    ws = None
-    flags = cpr.RUN_FUSED
-    if args.stepwise:
-        flags = cpr.RUN_STEPWISE
-        ws = torch.empty(cpr.cp_ring_attn_workspace_size(w.B, w.H, ri.lq, w.D), dtype=torch.uint8, device="cuda")
+    flags = cpr.RUN_STEPWISE if args.stepwise else cpr.RUN_FUSED
+    # the workspace holds the stepwise state, or the partial states of a fused run whose grid is too small
+    # for the GPU and is split over the keys (allocated before the timed region)
+    ws_bytes = cpr.cp_ring_attn_workspace_size(w.B, w.H, ri.lq, w.D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    kv_split = 1 if (args.stepwise or w.dtype != "bf16") else ws_bytes // (w.B * w.H * ri.lq * (w.D + 2) * 4)
     torch.cuda.synchronize()
     t_prep = time.perf_counter() - t_prep
 
@@ -365,7 +366,8 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic_from_profile(w.name),
-                "kernel": KERNEL_NAME if w.dtype == "bf16" else "attn_f32_kernel",
+                "kernel": (KERNEL_NAME if kv_split == 1 else f"{KERNEL_NAME} (keys split {kv_split} ways) + "
+                           "merge_finalize_kernel") if w.dtype == "bf16" else "attn_f32_kernel",
                 "kernel_ms": round(kernel_ms, 4), "flop_per_launch": flop}
 
     state_kernels = measure_state_kernels(cpr, torch, w.B, w.H, ri.lq, w.D, tdt, stream, q_local=ri.q_local,
@@ -393,6 +395,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H": w.H, "D": w.D, "seq_len": w.S, "cp_size": w.cp,
                    "layout": w.layout, "rank": rank, "causal": w.causal, "local_queries": ri.lq,
                    "allowed_pairs_per_bh": pairs, "run_mode": "stepwise" if args.stepwise else "fused",
+                   "kv_split": int(kv_split),
                    "input_prep_s": round(t_prep, 1)},
         "roofline": roofline,
         "state_kernels": state_kernels,

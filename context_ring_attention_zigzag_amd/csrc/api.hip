@@ -248,10 +248,17 @@ cpr_status cp_ring_attn_finalize(int32_t out_dtype, int32_t B, int32_t H, int32_
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// float32 state of `n` partial passes: O [n][rows][D], m [n][rows], l [n][rows], each 256-byte aligned
+static size_t state_bytes(size_t n, size_t rows, int32_t D) {
+  return round256(n * rows * D * sizeof(float)) + 2 * round256(n * rows * sizeof(float));
+}
+
 size_t cp_ring_attn_workspace_size(int32_t B, int32_t H, int32_t Lq, int32_t D) {
   if (B < 1 || H < 1 || Lq < 1 || (D != 64 && D != 128)) return 0;
   const size_t rows = (size_t)B * H * Lq;
-  return round256(rows * D * sizeof(float)) + 2 * round256(rows * sizeof(float));
+  // the stepwise state, or the partial states of a key-split fused run
+  const size_t split = (size_t)attn_bf16_kv_split(B, H, Lq, Lq);
+  return state_bytes(split > 1 ? split : 1, rows, D);
 }
 
 cpr_status cp_ring_attn_run(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t cp_size, int32_t rank,
@@ -280,17 +287,32 @@ cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, i
   const hipStream_t st = static_cast<hipStream_t>(stream);
   AttnArgs a = make_args(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, Lq, ring_pos, causal, softmax_scale,
                          ext);
+  const size_t rows = (size_t)B * H * Lq;
   if (flags == CPR_RUN_FUSED) {
     a.nblocks = cp_size; a.rank = rank; a.cp = cp_size;
+    // a grid too small for the chip is split over the keys when the caller's
+    // workspace holds the partial states; otherwise one launch does everything
+    const int32_t ns = dtype == CPR_BF16 ? attn_bf16_kv_split(B, H, Lq, Lq) : 1;
+    if (ns > 1 && workspace && workspace_bytes >= state_bytes(ns, rows, D) && aligned(workspace, 256)) {
+      char* w = static_cast<char*>(workspace);
+      a.o_acc = reinterpret_cast<float*>(w);
+      a.m = reinterpret_cast<float*>(w + round256(ns * rows * D * sizeof(float)));
+      a.l = reinterpret_cast<float*>(w + round256(ns * rows * D * sizeof(float)) + round256(ns * rows * sizeof(float)));
+      a.kv_split = ns; a.state_rows = (int64_t)rows;
+      a.load_state = 0; a.finalize = 0;
+      const hipError_t e = launch_attn(dtype, a, st);
+      if (e != hipSuccess) return hip_status(e, "cp_ring_attn_run");
+      return hip_status(launch_merge_finalize(1, ns, (int64_t)rows, D, a.o_acc, a.m, a.l, o_out, lse_out, st),
+                        "cp_ring_attn_run(merge)");
+    }
     a.o_out = o_out; a.lse = lse_out;
     a.load_state = 0; a.finalize = 1;
     return hip_status(launch_attn(dtype, a, st), "cp_ring_attn_run");
   }
-  const size_t need = cp_ring_attn_workspace_size(B, H, Lq, D);
+  const size_t need = state_bytes(1, rows, D);
   if (!workspace || workspace_bytes < need)
     return fail(CPR_EINVAL, "stepwise run needs a workspace of %zu bytes", need);
   if (!aligned(workspace, 256)) return fail(CPR_EINVAL, "workspace must be 256-byte aligned");
-  const size_t rows = (size_t)B * H * Lq;
   char* w = static_cast<char*>(workspace);
   float* o_acc = reinterpret_cast<float*>(w);
   float* m = reinterpret_cast<float*>(w + round256(rows * D * sizeof(float)));

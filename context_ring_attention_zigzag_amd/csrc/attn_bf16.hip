@@ -48,8 +48,13 @@
 //    skipped tiles are neither loaded nor computed, full tiles need no element
 //    mask;
 //  * the grid is remapped so that the workgroups of one (b, h) land on the
-//    same XCD (shared L2), heaviest query tiles first.
+//    same XCD (shared L2), heaviest query tiles first;
+//  * a grid too small to fill the chip is split over the keys: each query
+//    tile gets several workgroups, each walking one slice of every block's key
+//    tiles and writing its partial (O, m, l); a merge pass combines them.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "mfma_util.h"
@@ -85,7 +90,7 @@ struct Cfg {
 };
 
 
-template <int D, int NW>
+template <int D, int NW, bool SPLIT>
 __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   using C = Cfg<D, NW>;
   constexpr int kThreads = C::kThreads;
@@ -122,6 +127,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
     const int xcd = w % kXcds, idx = w / kXcds;
     const int per = ntiles / kXcds, rem = ntiles % kXcds;
     logical = xcd * per + min(xcd, rem) + idx;
+  }
+  int slice = 0;   // key slice of a split launch; its workgroups of one query tile are adjacent
+  if constexpr (SPLIT) {
+    slice = logical % a.kv_split;
+    logical /= a.kv_split;
   }
   const int bh = logical / nqt;
   const int qt = nqt - 1 - (logical - bh * nqt);
@@ -220,6 +230,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   const __bf16* kbh = static_cast<const __bf16*>(a.k) + b * a.k_sb + hk * a.k_sh;
   const __bf16* vbh = static_cast<const __bf16*>(a.v) + b * a.v_sb + hk * a.v_sh;
   const int n_kt = (a.Lk + kBN - 1) / kBN;
+  // key tiles of every block that this workgroup walks: all, or its slice
+  int kt_lo = 0, kt_hi = n_kt;
+  if constexpr (SPLIT) {
+    kt_lo = (int)((int64_t)slice * n_kt / a.kv_split);
+    kt_hi = (int)((int64_t)(slice + 1) * n_kt / a.kv_split);
+  }
 
   // LDS read offsets (elements), loop invariant.
   // K, A operand of S^T: lane (ql, hh) reads row 32*kt + ql, logical chunk 2*kk + hh.
@@ -255,8 +271,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
     const __bf16* kb = kbh + row0 * a.k_sl;
     const __bf16* vb = vbh + row0 * a.v_sl;
 
-    for (int seg0 = 0; seg0 < n_kt; seg0 += kMaxTiles) {
-      const int nseg = min(kMaxTiles, n_kt - seg0);
+    for (int seg0 = kt_lo; seg0 < kt_hi; seg0 += kMaxTiles) {
+      const int nseg = min(kMaxTiles, kt_hi - seg0);
 
       // ---- classify the segment's key tiles: 16 lanes per tile, 4 positions each
       bar();   // the previous segment is done with flags8 / klist / the buffers
@@ -605,7 +621,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   // a query that may attend no key position (a pad, or an empty window) has no
   // result even if it took part in an unmasked full tile
   const bool has = q_live && l_tot > 0.f;
-  if (a.finalize) {
+  if (!SPLIT && a.finalize) {
     const float inv = has ? 1.0f / l_tot : 0.f;
     __bf16* out = static_cast<__bf16*>(a.o_out) + srow * D;
 #pragma unroll
@@ -623,17 +639,18 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   } else {
     // hand back the state against the true running max: O and l scale by 2^(m_ref - m_true) <= 1
     const float beta = has ? __builtin_amdgcn_exp2f(m_ref - m_true) : 0.f;
+    const int64_t prow = SPLIT ? srow + (int64_t)slice * a.state_rows : srow;   // this slice's partial state
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float4 x = make_float4(ot[dt][4 * i + 0] * beta, ot[dt][4 * i + 1] * beta, ot[dt][4 * i + 2] * beta,
                                      ot[dt][4 * i + 3] * beta);
-        *reinterpret_cast<float4*>(a.o_acc + srow * D + 32 * dt + 8 * i + 4 * hh) = x;
+        *reinterpret_cast<float4*>(a.o_acc + prow * D + 32 * dt + 8 * i + 4 * hh) = x;
       }
     if (hh == 0) {
-      a.m[srow] = has ? m_true * kLn2 : -INFINITY;
-      a.l[srow] = has ? l_tot * beta : 0.f;
+      a.m[prow] = has ? m_true * kLn2 : -INFINITY;
+      a.l[prow] = has ? l_tot * beta : 0.f;
     }
   }
 }
@@ -641,12 +658,31 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
 template <int D, int NW>
 hipError_t launch(const AttnArgs& a, hipStream_t st) {
   const int nqt = (a.Lq + Cfg<D, NW>::kBM - 1) / Cfg<D, NW>::kBM;
-  const dim3 grid((unsigned)(nqt * a.B * a.H));
-  hipLaunchKernelGGL((attn_bf16_kernel<D, NW>), grid, dim3(NW * 64), 0, st, a);
+  if (a.kv_split > 1) {
+    const dim3 grid((unsigned)(nqt * a.B * a.H * a.kv_split));
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NW, true>), grid, dim3(NW * 64), 0, st, a);
+  } else {
+    const dim3 grid((unsigned)(nqt * a.B * a.H));
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NW, false>), grid, dim3(NW * 64), 0, st, a);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
+
+// Split only a grid that fills at most half of the 256 compute units, into as
+// many slices as bring it to about one workgroup per unit; a slice keeps at
+// least one key tile of every block.
+int32_t attn_bf16_kv_split(int32_t B, int32_t H, int32_t Lq, int32_t Lk) {
+  constexpr int64_t kCUs = 256, kMaxSplit = 16;
+  constexpr int kBM = Cfg<128, 8>::kBM;
+  static_assert(Cfg<64, 8>::kBM == kBM, "one query tile size");
+  if (B < 1 || H < 1 || Lq < 1 || Lk < 1) return 1;
+  const int64_t grid = (int64_t)((Lq + kBM - 1) / kBM) * B * H;
+  const int64_t n_kt = (Lk + kBN - 1) / kBN;
+  if (n_kt <= 1 || 2 * grid > kCUs) return 1;
+  return (int32_t)std::min(std::min(kCUs / grid, n_kt), kMaxSplit);
+}
 
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
   if (a.D == 64) return launch<64, 8>(a, st);

@@ -18,6 +18,10 @@ hipError_t launch_merge(int64_t rows, int32_t D, float* o, float* m, float* l, c
                         const float* m2, const float* l2, hipStream_t st);
 hipError_t launch_finalize(int out_bf16, int64_t rows, int32_t D, const float* o, const float* m,
                            const float* l, void* out, float* lse, hipStream_t st);
+// Merge of nsplit partial states (slice j at o + j * rows * D, m + j * rows,
+// l + j * rows) followed by finalize into (out, lse).
+hipError_t launch_merge_finalize(int out_bf16, int32_t nsplit, int64_t rows, int32_t D, const float* o,
+                                 const float* m, const float* l, void* out, float* lse, hipStream_t st);
 
 // Attention pass over `nblocks` KV blocks of Lk rows. Block t (t = 0..nblocks-1)
 // is block (rank - t) mod cp of the K/V/kv_pos buffers. State handling:
@@ -38,7 +42,19 @@ struct AttnArgs {
   float* o_acc; float* m; float* l;
   void* o_out; float* lse;
   int32_t load_state, finalize;
+  // split over the keys (bf16 path only): kv_split > 1 launches kv_split
+  // workgroups per query tile, slice j covering key tiles
+  // [j * n / kv_split, (j + 1) * n / kv_split) of every block (n = key tiles per
+  // block); each writes its partial state (o_acc, m, l) advanced by j slices of
+  // state_rows rows, and finalize / load_state are ignored
+  int32_t kv_split;
+  int64_t state_rows;
 };
+
+// Key slices per query tile (AttnArgs::kv_split) for a bf16 pass over Lq
+// queries of B*H heads and blocks of Lk keys: > 1 when the unsplit grid would
+// leave most of the chip idle, else 1.
+int32_t attn_bf16_kv_split(int32_t B, int32_t H, int32_t Lq, int32_t Lk);
 
 // Backward pass. Preprocessing, per query row: lse2 = LSE in log2 units (+inf
 // for a row that attends no key) and dvec = rowsum(dO * O); per query: qwin =

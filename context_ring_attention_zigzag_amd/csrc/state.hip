@@ -1,4 +1,5 @@
-// Running-state kernels: init, merge of two partial states, finalize.
+// Running-state kernels: init, merge of two partial states, finalize, and the
+// merge of a key-split launch's partial states fused with finalize.
 // All three are streaming passes over the float32 state and bound by HBM.
 //
 // The running max / running normaliser and the rescaling of earlier partial
@@ -111,6 +112,62 @@ hipError_t launch_finalize(int out_bf16, int64_t rows, int32_t D, const float* o
   else
     hipLaunchKernelGGL(finalize_kernel<false>, grid, dim3(256), 0, st, reinterpret_cast<const float4*>(o), m, l,
                        out, lse, rows, vpr);
+  return hipGetLastError();
+}
+
+// Merge of nsplit partial states over disjoint key sets, then finalize: per
+// row, m = max_j m_j, a_j = exp(m_j - m) (0 for an empty partial), l = sum_j
+// a_j l_j, O = sum_j a_j O_j / l, LSE = m + ln l; a row with l = 0 gives
+// O = 0, LSE = -inf. The same rescale rule as merge_kernel, over nsplit inputs.
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256) merge_finalize_kernel(const float4* __restrict__ o,
+                                                             const float* __restrict__ m,
+                                                             const float* __restrict__ l, void* __restrict__ out,
+                                                             float* __restrict__ lse, int32_t nsplit, int64_t rows,
+                                                             int32_t vpr) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= rows * vpr) return;
+  const int64_t r = g / vpr;
+  float mx = -INFINITY;
+  for (int j = 0; j < nsplit; ++j) mx = fmaxf(mx, m[j * rows + r]);
+  const float mu = (mx == -INFINITY) ? 0.f : mx;
+  float lt = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < nsplit; ++j) {
+    const float mj = m[j * rows + r];
+    const float aj = (mj == -INFINITY) ? 0.f : expf(mj - mu);
+    const float4 x = o[j * rows * vpr + g];
+    lt += aj * l[j * rows + r];
+    acc.x += aj * x.x;
+    acc.y += aj * x.y;
+    acc.z += aj * x.z;
+    acc.w += aj * x.w;
+  }
+  const bool has = lt > 0.f;
+  const float inv = has ? 1.0f / lt : 0.f;
+  const float4 y = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if constexpr (OUT_BF16) {
+    uint2 p;
+    p.x = f32_to_bf16_rne(y.x) | (f32_to_bf16_rne(y.y) << 16);
+    p.y = f32_to_bf16_rne(y.z) | (f32_to_bf16_rne(y.w) << 16);
+    reinterpret_cast<uint2*>(out)[g] = p;
+  } else {
+    reinterpret_cast<float4*>(out)[g] = y;
+  }
+  if (lse && g % vpr == 0) lse[r] = has ? mx + logf(lt) : -INFINITY;
+}
+
+hipError_t launch_merge_finalize(int out_bf16, int32_t nsplit, int64_t rows, int32_t D, const float* o,
+                                 const float* m, const float* l, void* out, float* lse, hipStream_t st) {
+  const int32_t vpr = D / 4;
+  const int64_t total = rows * vpr;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  if (out_bf16)
+    hipLaunchKernelGGL(merge_finalize_kernel<true>, grid, dim3(256), 0, st, reinterpret_cast<const float4*>(o), m,
+                       l, out, lse, nsplit, rows, vpr);
+  else
+    hipLaunchKernelGGL(merge_finalize_kernel<false>, grid, dim3(256), 0, st, reinterpret_cast<const float4*>(o), m,
+                       l, out, lse, nsplit, rows, vpr);
   return hipGetLastError();
 }
 

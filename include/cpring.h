@@ -74,7 +74,7 @@ typedef enum {
 
 /* Flags for cp_ring_attn_run. */
 enum {
-  CPR_RUN_FUSED = 0,    /* one launch walks every ring block; no workspace */
+  CPR_RUN_FUSED = 0,    /* one launch walks every ring block; optional workspace */
   CPR_RUN_STEPWISE = 1  /* init, cp calls of the step kernel, finalize; needs the workspace */
 };
 
@@ -172,8 +172,11 @@ cpr_status cp_ring_attn_finalize(int32_t out_dtype, int32_t B, int32_t H, int32_
                                  const float* o_acc, const float* m, const float* l,
                                  void* o_out, float* lse_out, void* stream);
 
-/* Workspace bytes cp_ring_attn_run needs with CPR_RUN_STEPWISE (the float32
- * state); CPR_RUN_FUSED needs none. Returns 0 for invalid sizes. */
+/* Workspace bytes for cp_ring_attn_run in either mode: the float32 state
+ * ([B,H,Lq,D] O, [B,H,Lq] m and l) that CPR_RUN_STEPWISE needs, or, for a bf16
+ * pass whose grid is too small to fill the GPU, the n partial states of a
+ * key-split CPR_RUN_FUSED run (n = 1 for large shapes, so the two coincide).
+ * Returns 0 for invalid sizes. */
 size_t cp_ring_attn_workspace_size(int32_t B, int32_t H, int32_t Lq, int32_t D);
 
 /*
@@ -187,7 +190,15 @@ size_t cp_ring_attn_workspace_size(int32_t B, int32_t H, int32_t Lq, int32_t D);
  * rank `rank` holds ("Context Parallelism", "How context parallelism works").
  * Writes o_out [B,H,Lq,D] (dtype, contiguous) and lse_out [B,H,Lq] (float32,
  * may be NULL). flags: CPR_RUN_FUSED or CPR_RUN_STEPWISE; the latter needs
- * `workspace` of cp_ring_attn_workspace_size() bytes (256-byte aligned).
+ * `workspace` of at least the float32 state's bytes (256-byte aligned; size it
+ * with cp_ring_attn_workspace_size()), else CPR_EINVAL. CPR_RUN_FUSED takes the
+ * workspace as an option: for a bf16 pass with too few query tiles to fill the
+ * GPU, a 256-byte-aligned workspace of cp_ring_attn_workspace_size() bytes lets
+ * it split every block's keys over several workgroups per query tile and
+ * merge their partial states (the running-max rescale rule of "Sequence
+ * Parallelism and Ring Attention", "Technical insight", over disjoint key
+ * sets); with no workspace, or a smaller one, it runs unsplit. The split
+ * changes only the float32 summation order.
  */
 cpr_status cp_ring_attn_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
                             int32_t cp_size, int32_t rank,

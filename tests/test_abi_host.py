@@ -164,6 +164,33 @@ def test_workspace_size(lib):
     assert lib.cp_ring_attn_workspace_size(1, 1, 1, 100) == 0
 
 
+def state_bytes(n, rows, D):
+    r256 = lambda x: (x + 255) // 256 * 256
+    return r256(n * rows * D * 4) + 2 * r256(n * rows * 4)
+
+
+@pytest.mark.parametrize("B,H,Lq,D,n", [
+    (2, 16, 8192, 128, 1),   # 1,024 query tiles of 256: fills the GPU, one state
+    (1, 32, 8192, 128, 1),   # 1,024
+    (1, 4, 2048, 64, 8),     # 32 query tiles: split 8 ways (256 / 32)
+    (1, 2, 250, 128, 4),     # 2 query tiles, but only 4 key tiles of 64 per block
+    (1, 1, 64, 128, 1),      # a single key tile per block: nothing to split
+    (1, 128, 256, 128, 2),   # 128 query tiles: half the GPU, split 2 ways
+    (1, 100, 256, 64, 2),    # 100 query tiles: split 2 ways
+    (1, 129, 256, 128, 1),   # 129 query tiles: more than half the GPU, no split
+    (1, 1, 100000, 64, 1),   # 391 query tiles of one head: no split
+])
+def test_workspace_size_covers_the_key_split(lib, B, H, Lq, D, n):
+    """The workspace holds n float32 states: n > 1 when a bf16 fused run splits the keys of a grid of at
+    most 128 query tiles (half of the 256 compute units) into min(256 // grid, key tiles per block, 16)
+    slices."""
+    grid = -(-Lq // 256) * B * H
+    n_kt = -(-Lq // 64)
+    expect = 1 if (2 * grid > 256 or n_kt <= 1) else min(256 // grid, n_kt, 16)
+    assert expect == n
+    assert lib.cp_ring_attn_workspace_size(B, H, Lq, D) == state_bytes(expect, B * H * Lq, D)
+
+
 def test_state_call_validation(lib):
     p = fake_ptr()
     assert lib.cp_ring_attn_init(1, 1, 0, 128, p, p, p, None) == cpr.EINVAL

@@ -23,6 +23,10 @@ from seeded_inputs import WORKLOADS, gen_slice, packed_windows, sample_rows, sma
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": (2e-2, 1e-3), "f32": (1e-5, 1e-5)}
+# third run mode of the tests: CPR_RUN_FUSED with a workspace, which splits
+# the keys of a bf16 pass whose grid is too small for the GPU
+SPLIT = "fused+workspace"
+MODES = (cpr.RUN_FUSED, cpr.RUN_STEPWISE, SPLIT)
 TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
@@ -71,10 +75,10 @@ def run_rank(w, dev, rank, flags):
     o = torch.empty_like(ri.q_local)
     lse = torch.empty(ri.q_local.shape[:3], dtype=torch.float32, device="cuda")
     ws = None
-    if flags == cpr.RUN_STEPWISE:
+    if flags in (cpr.RUN_STEPWISE, SPLIT):
         ws = torch.empty(cpr.cp_ring_attn_workspace_size(w.B, w.H, ri.lq, w.D), dtype=torch.uint8, device="cuda")
     cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, w.causal, 0.0, o, lse,
-                         ws, flags)
+                         ws, cpr.RUN_FUSED if flags == SPLIT else flags)
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), lse.cpu().numpy(), ri
 
@@ -130,7 +134,7 @@ def test_tiny_f32(flags):
         compare(o, lse, ro, rl, "f32", f"tiny_f32 r{r}")
 
 
-@pytest.mark.parametrize("flags", [cpr.RUN_FUSED, cpr.RUN_STEPWISE])
+@pytest.mark.parametrize("flags", MODES)
 def test_example_4k(flags):
     w = WORKLOADS["example_4k"]
     dev, host = natural_inputs(w)
@@ -167,7 +171,7 @@ def test_ragged_and_padded(case):
     dev, host = natural_inputs(w)
     lay = lay_code(w)
     for r in range(cp):
-        for flags in (cpr.RUN_FUSED, cpr.RUN_STEPWISE):
+        for flags in MODES:
             o, lse, _ = run_rank(w, dev, r, flags)
             ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], S, cp, lay, r, causal)
             compare(o, lse, ro, rl, dtype, f"{case} r{r} f{flags}")
@@ -181,7 +185,7 @@ def run_rank_ext(w, q_nat, k_nat, v_nat, rank, flags, lo_nat=None, hi_nat=None):
     o = torch.empty_like(ri.q_local)
     lse = torch.empty(ri.q_local.shape[:3], dtype=torch.float32, device="cuda")
     ws = None
-    if flags == cpr.RUN_STEPWISE:
+    if flags in (cpr.RUN_STEPWISE, SPLIT):
         ws = torch.empty(cpr.cp_ring_attn_workspace_size(w.B, w.H, ri.lq, w.D), dtype=torch.uint8, device="cuda")
     kw = [None, None]
     tok = ri.token_idx[rank * ri.lq:(rank + 1) * ri.lq].long()
@@ -191,7 +195,7 @@ def run_rank_ext(w, q_nat, k_nat, v_nat, rank, flags, lo_nat=None, hi_nat=None):
             nat_d = torch.from_numpy(np.asarray(nat, dtype=np.int32)).cuda()
             kw[i] = torch.where(real, nat_d[tok.clamp(max=w.S - 1)], 0).to(torch.int32).contiguous()
     cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, w.causal, 0.0, o, lse,
-                         ws, flags, kw_lo=kw[0], kw_hi=kw[1])
+                         ws, cpr.RUN_FUSED if flags == SPLIT else flags, kw_lo=kw[0], kw_hi=kw[1])
     torch.cuda.synchronize()
     return o.float().cpu().numpy(), lse.cpu().numpy()
 
@@ -214,7 +218,7 @@ def test_grouped_query_attention(case):
     hk, hv = host["k"][:, :H_kv], host["v"][:, :H_kv]
     for r in range(cp):
         ro, rl = oracle.rank_reference(host["q"], hk, hv, S, cp, ORACLE_LAYS[layout], r, causal)
-        for flags in (cpr.RUN_FUSED, cpr.RUN_STEPWISE):
+        for flags in MODES:
             o, lse = run_rank_ext(w, dev["q"], k_nat, v_nat, r, flags)
             compare(o, lse, ro, rl, dtype, f"{case} r{r} f{flags}")
 
@@ -238,7 +242,7 @@ def test_packed_documents(case):
     for r in range(cp):
         ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], S, cp, ORACLE_LAYS[layout], r, causal,
                                        kw_lo_nat=lo, kw_hi_nat=hi)
-        for flags in (cpr.RUN_FUSED, cpr.RUN_STEPWISE):
+        for flags in MODES:
             o, lse = run_rank_ext(w, dev["q"], dev["k"], dev["v"], r, flags, lo, hi)
             compare(o, lse, ro, rl, dtype, f"{case[:6]} r{r} f{flags}")
 
@@ -254,7 +258,7 @@ def test_sliding_window_with_empty_windows():
         ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], w.S, w.cp, oracle.ZIGZAG, r, True,
                                        kw_lo_nat=lo, kw_hi_nat=hi)
         assert np.isneginf(rl).any()
-        for flags in (cpr.RUN_FUSED, cpr.RUN_STEPWISE):
+        for flags in MODES:
             o, lse = run_rank_ext(w, dev["q"], dev["k"], dev["v"], r, flags, lo, hi)
             compare(o, lse, ro, rl, "bf16", f"window r{r} f{flags}")
 
@@ -451,6 +455,33 @@ def test_run_is_deterministic():
     a, la, _ = run_rank(w, dev, 1, cpr.RUN_FUSED)
     b, lb, _ = run_rank(w, dev, 1, cpr.RUN_FUSED)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_key_split_engages_and_matches():
+    """The 4,096-token example has 32 query tiles of 256 for 256 compute units: a fused run with a workspace
+    splits every block's keys 8 ways. The workspace (poisoned with NaN first) must then hold the 8 partial
+    states; the result matches the oracle and is bit-reproducible."""
+    w = WORKLOADS["example_4k"]
+    dev, host = natural_inputs(w)
+    ri = di.prepare_rank(dev["q"], dev["k"], dev["v"], w.S, w.cp, lay_code(w), 0)
+    rows = w.B * w.H * ri.lq
+    size = cpr.cp_ring_attn_workspace_size(w.B, w.H, ri.lq, w.D)
+    ns = size // (rows * (w.D + 2) * 4)
+    assert size == ns * rows * (w.D + 2) * 4 and ns == 8
+    outs = []
+    for _ in range(2):
+        ws = torch.full((size // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        o = torch.empty_like(ri.q_local)
+        lse = torch.empty(ri.q_local.shape[:3], dtype=torch.float32, device="cuda")
+        cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, 0, True, 0.0, o, lse,
+                             ws, cpr.RUN_FUSED)
+        torch.cuda.synchronize()
+        m_parts = ws[ns * rows * w.D: ns * rows * (w.D + 1)]
+        assert not torch.isnan(m_parts).any(), "the partial states were not written"
+        outs.append((o.float().cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
+    ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], w.S, w.cp, oracle.ZIGZAG, 0, True)
+    compare(outs[0][0], outs[0][1], ro, rl, "bf16", "example_4k key split")
 
 
 def test_fused_and_stepwise_agree():
