@@ -108,10 +108,12 @@ def cpu_baseline(w, rank: int, budget_s: float):
 
 def measure_state_kernels(cpr, torch, B: int, H: int, Lq: int, D: int, out_dtype, stream, reps: int = 10,
                           q_local=None, q_pos=None):
-    """HBM throughput of the finalize, merge and rotary-embedding kernels at the workload's local shape.
+    """HBM throughput of the state-init, finalize, merge and rotary-embedding kernels at the workload's
+    local shape.
 
-    Algorithmic bytes per row: finalize reads O (4D) + m, l (8) and writes O (D*esize) + LSE (4);
-    merge reads two states (8D + 16) and writes one (4D + 8); the rotary embedding of the rank's queries
+    Algorithmic bytes per row: state init writes O (4D) + m, l (8); finalize reads O (4D) + m, l (8) and
+    writes O (D*esize) + LSE (4); merge reads two states (8D + 16) and writes one (4D + 8); the rotary
+    embedding of the rank's queries
     by their global positions reads and writes one row (2*D*esize) plus its position (4 bytes per row of
     one (b, h)).
     """
@@ -129,6 +131,8 @@ def measure_state_kernels(cpr, torch, B: int, H: int, Lq: int, D: int, out_dtype
               rows * (4 * D + 8 + D * esize + 4)),
              ("merge_kernel", lambda: cpr.cp_ring_attn_merge(o, m, l, o2, m2, l2, stream),
               rows * (8 * D + 16 + 4 * D + 8))]
+    o3, m3, l3 = torch.empty_like(o), torch.empty_like(m), torch.empty_like(l)
+    cases.append(("state_init_kernel", lambda: cpr.cp_ring_attn_init(o3, m3, l3, stream), rows * (4 * D + 8)))
     if q_local is not None:
         cases.append(("rope_kernel", lambda: cpr.cp_rope_apply(q_local, q_pos, out=out, stream=stream),
                       rows * 2 * D * esize + Lq * 4))
