@@ -50,17 +50,28 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_from_profile(workload: str):
-    """HBM bytes per launch from the committed counter summary, if it matches the current kernel."""
-    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_traffic.md")
+def field_from_profile(workload: str, kind: str, field: str):
+    """A machine-readable field of a committed counter summary, if the summary matches the current kernel."""
+    path = os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}_{kind}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+    m_val = re.search(field + r":\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_hash():
         return None
-    return float(m_bytes.group(1))
+    return float(m_val.group(1))
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) of the current kernel, or None."""
+    return field_from_profile(workload, "traffic", "hbm_bytes_per_launch")
+
+
+def mfma_busy_from_profile(workload: str):
+    """Fraction of the kernel's cycles in which the matrix cores are busy (SQ_VALU_MFMA_BUSY_CYCLES per
+    SIMD over GRBM_GUI_ACTIVE per XCD) of the current kernel, or None."""
+    return field_from_profile(workload, "counters", "mfma_busy_frac")
 
 
 def cpu_baseline(w, rank: int, budget_s: float):
@@ -372,7 +383,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic_from_profile(w.name),
                 "kernel": (KERNEL_NAME if kv_split == 1 else f"{KERNEL_NAME} (keys split {kv_split} ways) + "
                            "merge_finalize_kernel") if w.dtype == "bf16" else "attn_f32_kernel",
-                "kernel_ms": round(kernel_ms, 4), "flop_per_launch": flop}
+                "kernel_ms": round(kernel_ms, 4), "flop_per_launch": flop,
+                "mfma_busy_frac": mfma_busy_from_profile(w.name) if kv_split == 1 else None}
 
     state_kernels = measure_state_kernels(cpr, torch, w.B, w.H, ri.lq, w.D, tdt, stream, q_local=ri.q_local,
                                           q_pos=ri.q_pos)
