@@ -106,6 +106,11 @@ struct RowFrags {
   __device__ __forceinline__ bf16x8 get(const __bf16* tile, int kk) const {
     return *reinterpret_cast<const bf16x8*>(tile + off[kk]);
   }
+  // move every offset by d elements (to another tile buffer of the same array)
+  __device__ __forceinline__ void shift(int d) {
+#pragma unroll
+    for (int kk = 0; kk < BCfg<D>::kKSteps; ++kk) off[kk] += d;
+  }
 };
 
 // A-operand fragments of the transposed tile through two transposed reads:
@@ -130,6 +135,14 @@ struct TrFrags {
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off[0][dt] + 16 * c * D));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off[1][dt] + 16 * c * D));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+  // see RowFrags::shift
+  __device__ __forceinline__ void shift(int d) {
+#pragma unroll
+    for (int dt = 0; dt < BCfg<D>::kDTiles; ++dt) {
+      off[0][dt] += d;
+      off[1][dt] += d;
+    }
   }
 };
 
@@ -516,6 +529,7 @@ constexpr int kKvMaxTiles = 8 * kKvThreads;   // query tiles classified per segm
 template <int D>
 __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
   using C = BCfg<D>;
+  constexpr int kTileElems = kT * D;   // elements of one streamed tile buffer
   constexpr int kLoads = C::kTileLoads / 2;   // per role-A wave: two waves per tensor
   static_assert(kLoads >= 1 && C::kTileLoads % 2 == 0, "tile/waves mismatch");
 
@@ -709,8 +723,9 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
         constexpr bool kS = decltype(ws)::value, kV = decltype(wv)::value;
         constexpr int kNs = kS ? C::kKSteps : 0;
         constexpr int kN = kNs + (kV ? 2 * C::kDTiles : 0);
-        const __bf16* qt_l = &q_lds[k % 3][0];
-        const __bf16* gt_l = &g_lds[(k + 2) % 3][0];
+        // rowf points at buffer k % 3 (Q(k)), trf at buffer (k - 1) % 3 (dO(k - 1))
+        const __bf16* qt_l = &q_lds[0][0];
+        const __bf16* gt_l = &g_lds[0][0];
         const bool more = k + 1 < nitems;
         const Plan pl = plan(more ? k + 1 : k);
         // load n of item k + 1 goes out after MFMA 1 + 3n: the address unit
@@ -775,8 +790,9 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       auto b_mfma = [&](int k, auto wp, auto wk) __attribute__((always_inline)) {
         constexpr bool kP = decltype(wp)::value, kK = decltype(wk)::value;
         constexpr int kNp = kP ? C::kKSteps : 0;
-        const __bf16* gt_l = &g_lds[k % 3][0];
-        const __bf16* qt_l = &q_lds[(k + 2) % 3][0];
+        // rowf points at buffer k % 3 (dO(k)), trf at buffer (k - 1) % 3 (Q(k - 1))
+        const __bf16* gt_l = &g_lds[0][0];
+        const __bf16* qt_l = &q_lds[0][0];
         mfma_stream<kNp + (kK ? 2 * C::kDTiles : 0), kK ? 2 : 1>(
             [&](int m) {
               if (m < kNp) return rowf.get(gt_l, m);
@@ -814,6 +830,14 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       // last (k = nitems) have no previous or no current item
       auto phases = [&](int k, auto first, auto last) __attribute__((always_inline)) {
         constexpr bool kFirst = decltype(first)::value, kLast = decltype(last)::value;
+        // advance the fragment offsets one buffer: rowf to k % 3, trf to (k - 1) % 3 (back by two at
+        // the wrap), so that every operand read of the matrix phases is a lane register plus an
+        // immediate offset
+        if (!kFirst) {
+          const int sk = k % 3;
+          rowf.shift(sk == 0 ? -2 * kTileElems : kTileElems);
+          trf.shift(sk == 1 ? -2 * kTileElems : kTileElems);
+        }
         // phase 2k: A on the matrix cores, B on the vector ALU (+ loads of item k + 1)
         if (kA) {
           a_mfma(k, std::integral_constant<bool, !kLast>{}, std::integral_constant<bool, !kFirst>{});
@@ -834,6 +858,10 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
         bar();
       };
 
+      // fragment offsets of item 0: rowf at buffer 0, trf at buffer 2 (= (0 - 1) mod 3)
+      rowf.init(ql, hh);
+      trf.init(lane);
+      trf.shift(2 * kTileElems);
       // prologue: item 0 in LDS
       if (kA) {
         const Plan p0 = plan(0);
