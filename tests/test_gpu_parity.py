@@ -484,6 +484,27 @@ def test_key_split_engages_and_matches():
     compare(outs[0][0], outs[0][1], ro, rl, "bf16", "example_4k key split")
 
 
+@pytest.mark.parametrize("how", ["one byte short", "misaligned"])
+def test_key_split_needs_a_whole_aligned_workspace(how):
+    """A fused run whose workspace is one byte too small, or not 256-byte aligned, runs unsplit: it leaves
+    the (NaN-poisoned) workspace untouched and still matches the oracle."""
+    w = WORKLOADS["example_4k"]
+    dev, host = natural_inputs(w)
+    ri = di.prepare_rank(dev["q"], dev["k"], dev["v"], w.S, w.cp, lay_code(w), 1)
+    size = cpr.cp_ring_attn_workspace_size(w.B, w.H, ri.lq, w.D)
+    buf = torch.full((size // 4 + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    ws = buf[: size // 4].view(torch.uint8)[: size - 1] if how == "one byte short" else buf[4: 4 + size // 4]
+    assert (ws.data_ptr() % 256 != 0) == (how == "misaligned")
+    o = torch.empty_like(ri.q_local)
+    lse = torch.empty(ri.q_local.shape[:3], dtype=torch.float32, device="cuda")
+    cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, 1, True, 0.0, o, lse, ws,
+                         cpr.RUN_FUSED)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf).all(), "an unsplit run must not write the workspace"
+    ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], w.S, w.cp, oracle.ZIGZAG, 1, True)
+    compare(o.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, "bf16", f"example_4k unsplit ({how})")
+
+
 def test_fused_and_stepwise_agree():
     w = small_workload("agree", "bf16", 1, 2, 128, 8192, 4, "zigzag", True, seed=10)
     dev, _ = natural_inputs(w)
