@@ -200,7 +200,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   f32x16 ot[C::kDTiles];
   float m_ref = -INFINITY, m_true = -INFINITY, lsum0 = 0.f, lsum1 = 0.f;
   const int64_t srow = (int64_t)bh * a.Lq + q_idx;
-  if (a.load_state && q_in) {
+  if (!SPLIT && a.load_state && q_in) {   // a split launch always starts from an empty state
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
