@@ -400,6 +400,37 @@ def test_million_cp8_sampled():
     sampled_check("million_cp8", cpr.RUN_FUSED, n_rows=40)
 
 
+def test_seq32k_grouped_heads_packed_documents_sampled():
+    """The 32k-token zigzag share (rank 3 of 4) with 32 query heads over 8 K/V heads and five packed
+    documents of uneven length: sampled rows against the oracle in the fused and stepwise modes."""
+    H, H_kv, group = 32, 8, 4
+    w = small_workload("gqa_docs_32k", "bf16", 1, H, 128, 32768, 4, "zigzag", True, seed=31, ranks=(3,))
+    docs = (5000, 12000, 768, 9000, 6000)
+    assert sum(docs) == w.S
+    lo, hi = packed_windows(docs, True)
+    lq = w.S // w.cp
+    rows = sample_rows(lq, lq // 2, 64, seed=w.seed)
+    q_nat = torch.empty((1, H, w.S, w.D), dtype=torch.bfloat16, device="cuda")
+    k_nat = torch.empty((1, H_kv, w.S, w.D), dtype=torch.bfloat16, device="cuda")
+    v_nat = torch.empty_like(k_nat)
+    ro = np.zeros((1, H, len(rows), w.D))
+    rl = np.zeros((1, H, len(rows)))
+    for g in range(H_kv):
+        kv = {t: gen_slice(w, t, 0, g) for t in "kv"}
+        k_nat[0, g].copy_(torch.from_numpy(kv["k"]).to(torch.bfloat16))
+        v_nat[0, g].copy_(torch.from_numpy(kv["v"]).to(torch.bfloat16))
+        qs = np.stack([gen_slice(w, "q", 0, h) for h in range(g * group, (g + 1) * group)])
+        q_nat[0, g * group:(g + 1) * group].copy_(torch.from_numpy(qs).to(torch.bfloat16))
+        o_g, l_g = oracle.rank_reference(qs[None].astype(np.float64), kv["k"][None, None].astype(np.float64),
+                                         kv["v"][None, None].astype(np.float64), w.S, w.cp, oracle.ZIGZAG, 3, True,
+                                         rows=rows, kw_lo_nat=lo, kw_hi_nat=hi)
+        ro[0, g * group:(g + 1) * group], rl[0, g * group:(g + 1) * group] = o_g[0], l_g[0]
+    for flags in (cpr.RUN_FUSED, cpr.RUN_STEPWISE):
+        note(f"gqa_docs_32k rank 3 flags {flags}")
+        o, lse = run_rank_ext(w, q_nat, k_nat, v_nat, 3, flags, lo, hi)
+        compare(o[:, :, rows], lse[:, :, rows], ro, rl, "bf16", f"gqa_docs_32k f{flags} (sampled)")
+
+
 def test_million_cp8_zero_keys_closed_form_all_rows():
     """K = 0 at full size: every allowed score is 0, so LSE = ln(#allowed keys)
     and O = mean of V over the allowed prefix, for every local row."""
