@@ -168,6 +168,15 @@ def test_bwd_packed_documents(dtype):
     run_case(c, (0, 3), f"{dtype}_docs")
 
 
+def test_bwd_mid_size_grouped_heads_documents_padded():
+    """8,190 tokens (padded to 8,192) over 4 zigzag ranks, 8 query heads on 2 K/V heads, five packed documents:
+    many key and query tiles per workgroup, a padded tail, windows and head groups together, compared in full
+    with the oracle's ring backward."""
+    docs = [1000, 3000, 190, 2500, 1500]
+    c = Case("bf16", 1, 8, 2, 128, sum(docs), 4, "zigzag", True, seed=310, docs=docs)
+    run_case(c, (0, 3), "bf16_mid_gqa_docs")
+
+
 def test_bwd_large_scores():
     """Scores spread over a wide range (scaled Q and K): the saved LSE makes P exact at any scale."""
     c = Case("bf16", 1, 2, 2, 128, 2048, 2, "zigzag", True, seed=307, scale=3.0)
