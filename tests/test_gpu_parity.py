@@ -247,6 +247,26 @@ def test_packed_documents(case):
             compare(o, lse, ro, rl, dtype, f"{case[:6]} r{r} f{flags}")
 
 
+@pytest.mark.parametrize("layout", ["zigzag", "striped"])
+def test_mid_size_grouped_heads_documents_padded(layout):
+    """8,190 tokens (padded) over 4 ranks, 8 query heads on 2 K/V heads, five packed documents: many tiles, a
+    padded tail, windows and head groups together, every row compared in the fused, stepwise and key-split
+    modes (the split engages here: 64 query tiles for 256 compute units)."""
+    docs = (1000, 3000, 190, 2500, 1500)
+    H, H_kv = 8, 2
+    w = small_workload("mid", "bf16", 1, H, 128, sum(docs), 4, layout, True, seed=41)
+    dev, host = natural_inputs(w)
+    k_nat, v_nat = dev["k"][:, :H_kv].contiguous(), dev["v"][:, :H_kv].contiguous()
+    hk, hv = host["k"][:, :H_kv], host["v"][:, :H_kv]
+    lo, hi = packed_windows(docs, True)
+    for r in (0, 3):
+        ro, rl = oracle.rank_reference(host["q"], hk, hv, w.S, w.cp, ORACLE_LAYS[layout], r, True,
+                                       kw_lo_nat=lo, kw_hi_nat=hi)
+        for flags in MODES:
+            o, lse = run_rank_ext(w, dev["q"], k_nat, v_nat, r, flags, lo, hi)
+            compare(o, lse, ro, rl, "bf16", f"mid {layout} r{r} f{flags}")
+
+
 def test_sliding_window_with_empty_windows():
     """Causal window of 100 keys; every 7th query gets an empty window (hi < lo): O = 0, LSE = -inf there."""
     w = small_workload("window", "bf16", 1, 2, 128, 1500, 4, "zigzag", True, seed=21)
