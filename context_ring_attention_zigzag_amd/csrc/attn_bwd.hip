@@ -22,15 +22,14 @@
 //    bank conflicts: the row reads of an A operand (16 lanes, 16 rows, one
 //    chunk) and the transposed reads (ds_read_b64_tr_b16: 16 lanes, 4 rows, two
 //    chunks) that give the tile's transpose as an A operand;
-//  * the dQ kernel: a workgroup owns 256 queries of one (b, h) (D = 128: eight
-//    waves, one workgroup per CU, so the CU keeps one LDS copy of each key
-//    tile; D = 64: 128 queries, two workgroups per CU), each wave 32 of
+//  * the dQ kernel: a workgroup owns 128 queries of one (b, h), each wave 32 of
 //    them with Q and dO resident in VGPRs in the B-operand layout of
 //    v_mfma_f32_32x32x16_bf16. Keys stream through LDS in tiles of 32 with
 //    direct buffer->LDS loads, double-buffered. S^T = K Q^T and dP^T = V dO^T
 //    put one query and 16 keys in each lane, so P^T and dS^T are lane-local and
 //    leave the accumulators already in the B-operand layout of
-//    dQ^T += K^T dS^T (v_cvt_pk_bf16_f32, round to nearest even);
+//    dQ^T += K^T dS^T (v_cvt_pk_bf16_f32, round to nearest even); two
+//    workgroups share a CU;
 //  * the dK/dV kernel: a workgroup owns 128 keys of one (b, kv head) as four
 //    pairs of waves, 32 keys per pair, and streams query tiles (Q, dO, lse2,
 //    Dvec, windows) of every query head of the grouped-query group through
@@ -255,18 +254,13 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdPrepArgs a) {
 
 // ---------------------------------------------------------------- dQ kernel
 
-// Waves per dQ workgroup, 32 queries each: eight for D = 128, so that the eight
-// waves of a compute unit share one LDS copy of every key tile; four for
-// D = 64 (two workgroups per unit), whose tile has too few 16-byte loads for
-// eight waves.
-template <int D>
-constexpr int kQWavesFor = D == 128 ? 8 : 4;
+constexpr int kQWaves = 4;                    // 32 queries each
+constexpr int kQThreads = 64 * kQWaves;
+constexpr int kQOwn = 32 * kQWaves;           // queries per workgroup
+constexpr int kQMaxTiles = 8 * kQThreads;     // key tiles classified per segment
 
-template <int D, int kQWaves = kQWavesFor<D>>
-__global__ void __launch_bounds__(64 * kQWaves, 8 / kQWaves) bwd_dq_kernel(BwdArgs a) {
-  constexpr int kQThreads = 64 * kQWaves;
-  constexpr int kQOwn = 32 * kQWaves;           // queries per workgroup
-  constexpr int kQMaxTiles = 8 * kQThreads;     // key tiles classified per segment
+template <int D>
+__global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
   using C = BCfg<D>;
   constexpr int kLoads = C::kTileLoads / kQWaves;   // per wave per tensor
   static_assert(kLoads >= 1 && C::kTileLoads % kQWaves == 0, "tile/waves mismatch");
@@ -910,9 +904,8 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
 template <int D>
 hipError_t launch_bwd(const BwdArgs& a, int32_t do_dq, int32_t do_dkv, hipStream_t st) {
   if (do_dq) {
-    constexpr int kQOwn = 32 * kQWavesFor<D>;
     const int nqt = (a.Lq + kQOwn - 1) / kQOwn;
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nqt * a.B * a.H)), dim3(64 * kQWavesFor<D>), 0, st, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nqt * a.B * a.H)), dim3(kQThreads), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
