@@ -372,8 +372,10 @@ def test_finalize_and_init_kernels(dtype):
 # ------------------------------------------------- full-size workloads
 
 def sampled_check(name, flags=cpr.RUN_FUSED, n_rows=None):
-    """Run the workload's rank(s) on the GPU; compare sampled rows with the oracle head by head."""
-    w = WORKLOADS[name]
+    """Run the workload's rank(s) on the GPU; compare sampled rows with the oracle head by head.
+    ``name`` is a workload name or a Workload."""
+    w = WORKLOADS[name] if isinstance(name, str) else name
+    name = w.name
     lay = lay_code(w)
     olay = ORACLE_LAYS[w.layout]
     s_pad = oracle.padded_len(w.S, w.cp, olay)
@@ -414,6 +416,13 @@ def test_seq32k_cp4_stepwise_sampled():
 
 def test_longdoc_noncausal_sampled():
     sampled_check("longdoc_noncausal", cpr.RUN_FUSED, n_rows=64)
+
+
+def test_noncausal_64k_head_dim_64_sampled():
+    """The non-causal 65,536-token share at head dimension 64 (the D = 64 kernel at a large shape)."""
+    w = small_workload("longdoc_d64", "bf16", 2, 16, 64, 65536, 8, "contiguous", False, seed=42, ranks=(0,),
+                       input_scale=0.5)
+    sampled_check(w, cpr.RUN_FUSED, n_rows=48)
 
 
 def test_million_cp8_sampled():
