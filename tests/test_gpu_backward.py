@@ -168,13 +168,14 @@ def test_bwd_packed_documents(dtype):
     run_case(c, (0, 3), f"{dtype}_docs")
 
 
-def test_bwd_mid_size_grouped_heads_documents_padded():
+@pytest.mark.parametrize("d", [128, 64])
+def test_bwd_mid_size_grouped_heads_documents_padded(d):
     """8,190 tokens (padded to 8,192) over 4 zigzag ranks, 8 query heads on 2 K/V heads, five packed documents:
     many key and query tiles per workgroup, a padded tail, windows and head groups together, compared in full
-    with the oracle's ring backward."""
+    with the oracle's ring backward, at both head dimensions."""
     docs = [1000, 3000, 190, 2500, 1500]
-    c = Case("bf16", 1, 8, 2, 128, sum(docs), 4, "zigzag", True, seed=310, docs=docs)
-    run_case(c, (0, 3), "bf16_mid_gqa_docs")
+    c = Case("bf16", 1, 8, 2, d, sum(docs), 4, "zigzag", True, seed=310 + d, docs=docs)
+    run_case(c, (0, 3), f"bf16_mid_gqa_docs_d{d}")
 
 
 def test_bwd_large_scores():
