@@ -198,7 +198,9 @@ size_t cp_ring_attn_workspace_size(int32_t B, int32_t H, int32_t Lq, int32_t D);
  * merge their partial states (the running-max rescale rule of "Sequence
  * Parallelism and Ring Attention", "Technical insight", over disjoint key
  * sets); with no workspace, or a smaller one, it runs unsplit. The split
- * changes only the float32 summation order.
+ * changes only the float32 summation order. In either mode the workspace is
+ * scratch that the call overwrites: calls in flight at the same time must not
+ * share one.
  */
 cpr_status cp_ring_attn_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
                             int32_t cp_size, int32_t rank,
