@@ -41,12 +41,17 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 
 int esize_of(int32_t dtype) { return dtype == CPR_BF16 ? 2 : 4; }
 
-// A [B, H, L, D] view with D contiguous.
-cpr_status check_view(const char* name, const cpr_view* v, int32_t dtype) {
+// A [B, H, L, D] view with D contiguous. Rows must not overlap (stride_l >= D):
+// the kernels address a block of rows as one byte range of rows * stride_l
+// elements, which holds every row only when no two of them share memory.
+cpr_status check_view(const char* name, const cpr_view* v, int32_t dtype, int32_t D) {
   if (!v) return fail(CPR_EINVAL, "%s: view pointer is NULL", name);
   if (!v->data) return fail(CPR_EINVAL, "%s: data pointer is NULL", name);
   if (v->stride_b < 0 || v->stride_h < 0 || v->stride_l < 0)
     return fail(CPR_EINVAL, "%s: negative stride", name);
+  if (v->stride_l < D)
+    return fail(CPR_EUNSUPPORTED, "%s: stride_l = %lld is below D = %d (overlapping rows)", name,
+                (long long)v->stride_l, D);
   if (v->stride_l > ((int64_t)1 << 24)) return fail(CPR_EUNSUPPORTED, "%s: stride_l must be <= 2^24", name);
   const int64_t align_elems = dtype == CPR_BF16 ? 8 : 1;   // 16-byte rows for bf16
   if (dtype == CPR_BF16) {
@@ -127,7 +132,7 @@ cpr_status cp_shard_gather(int32_t dtype, int32_t B, int32_t H, int64_t seq_len,
   TRY(check_dims(dtype, B, H, D));
   TRY(check_len("seq_len", seq_len));
   TRY(check_len("n_out", n_out));
-  TRY(check_view("src", src, dtype));
+  TRY(check_view("src", src, dtype, D));
   if (dtype == CPR_F32) {
     if (!aligned(src->data, 16) || src->stride_b % 4 || src->stride_h % 4 || src->stride_l % 4)
       return fail(CPR_EINVAL, "src: f32 gather needs 16-byte aligned rows");
@@ -164,9 +169,9 @@ static cpr_status validate_attn(int32_t dtype, int32_t B, int32_t H, int32_t D, 
   }
   TRY(check_len("Lq", Lq));
   TRY(check_len("KV length", Lk_total));
-  TRY(check_view("q", q, dtype));
-  TRY(check_view("k", k, dtype));
-  TRY(check_view("v", v, dtype));
+  TRY(check_view("q", q, dtype, D));
+  TRY(check_view("k", k, dtype, D));
+  TRY(check_view("v", v, dtype, D));
   if ((need_q_pos && !q_pos) || !kv_pos) return fail(CPR_EINVAL, "position arrays must be non-NULL");
   TRY(check_grid(B, H, Lq));
   TRY(check_grid(B, ext && ext->H_kv > 0 ? ext->H_kv : H, (int32_t)Lk_total));   // Lk_total <= 2^30 here
@@ -372,8 +377,8 @@ cpr_status cp_ring_attn_bwd_prep(int32_t dtype, int32_t B, int32_t H, int32_t D,
                                  void* workspace, size_t workspace_bytes, void* stream) {
   TRY(check_dims(dtype, B, H, D));
   TRY(check_len("Lq", Lq));
-  TRY(check_view("o_local", o_local, dtype));
-  TRY(check_view("do_local", do_local, dtype));
+  TRY(check_view("o_local", o_local, dtype, D));
+  TRY(check_view("do_local", do_local, dtype, D));
   TRY(check_rows16("o_local", o_local, dtype));
   TRY(check_rows16("do_local", do_local, dtype));
   if (!lse_local || !aligned(lse_local, 4)) return fail(CPR_EINVAL, "lse_local must be non-NULL and 4-byte aligned");
@@ -425,7 +430,7 @@ cpr_status cp_ring_attn_bwd_step(int32_t dtype, int32_t B, int32_t H, int32_t D,
                                  float* dq_acc, float* dk_acc, float* dv_acc, void* stream) {
   cpr_attn_ext ext{H_kv, nullptr, nullptr};
   TRY(validate_attn(dtype, B, H, D, q, Lq, nullptr, k, v, Lk, kv_pos, &ext, /*need_q_pos=*/0));
-  TRY(check_view("dout", dout, dtype));
+  TRY(check_view("dout", dout, dtype, D));
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(CPR_EINVAL, "softmax_scale must be finite");
   TRY(check_bwd_workspace(B, H, Lq, workspace, workspace_bytes));
@@ -473,7 +478,7 @@ cpr_status cp_rope_apply(int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t
                          const int32_t* pos, float base, int32_t style, void* out, void* stream) {
   TRY(check_dims(dtype, B, H, D));
   TRY(check_len("L", L));
-  TRY(check_view("x", x, dtype));
+  TRY(check_view("x", x, dtype, D));
   TRY(check_rows16("x", x, dtype));
   if (!pos) return fail(CPR_EINVAL, "pos is NULL");
   if (!(base > 0.f) || isinf(base)) return fail(CPR_EINVAL, "base must be positive and finite");

@@ -21,8 +21,10 @@
  * Conventions shared by every call:
  *  - Tensors are [B, H, L, D] (sequence on dim 2, as in the SDPA call on the
  *    glossary page, "Practical use and trade-offs"). A cpr_view gives element
- *    strides for B, H and L; the D dimension must be contiguous. Views of
- *    bf16 tensors need every stride and the base address 16-byte aligned.
+ *    strides for B, H and L; the D dimension must be contiguous and rows may
+ *    not overlap (stride_l >= D, else CPR_EUNSUPPORTED; B and H strides may
+ *    be 0 for a broadcast input). Views of bf16 tensors need every stride and
+ *    the base address 16-byte aligned.
  *  - Every pointer argument named as device memory must point to memory of
  *    the current HIP device; position arrays are int32 device arrays.
  *  - The caller owns every buffer. The library never allocates or frees
@@ -165,6 +167,11 @@ cpr_status cp_ring_attn_merge(int32_t B, int32_t H, int32_t Lq, int32_t D,
 /*
  * Normalise the state after the last step: o_out = O / l, rounded to nearest
  * even in out_dtype (CPR_BF16 or CPR_F32), and lse_out = m + ln l (float32).
+ * The running normaliser l and max m are those of "Sequence Parallelism and
+ * Ring Attention", "Technical insight": dividing the unnormalised sum by l
+ * once every block is folded in gives the softmax-weighted output, which
+ * "Context Parallelism", "How context parallelism works", states equals
+ * full-sequence attention.
  * Rows with l = 0 give O = 0, LSE = -inf. o_out is a contiguous [B,H,Lq,D]
  * device buffer, lse_out a contiguous [B,H,Lq] float32 buffer (may be NULL).
  */

@@ -20,10 +20,11 @@ Pages this oracle follows (cited by title and section):
 
 Every function here is pinned by ``tests/test_oracle.py`` to something other
 than itself (brute force, a library routine, closed forms, the pages' cp=4
-table). No function is "parity unpinned".
+table; the rotary frequencies theta_j by hand-computed angles for every pair
+j, checked with scalar math.cos / math.sin). No function is "parity unpinned".
 """
 
-from .rope import HALF, INTERLEAVED, rope, rope_pairs  # noqa: F401
+from .rope import HALF, INTERLEAVED, rope, rope_pairs, rope_theta  # noqa: F401
 from .ring_attention import (  # noqa: F401
     CONTIGUOUS,
     STRIPED,

@@ -33,6 +33,11 @@ def rope_pairs(d: int, style: int):
     raise ValueError("unknown rotary style")
 
 
+def rope_theta(d: int, base: float):
+    """Angular frequency of each pair: theta_j = base^(-2j/D), j = 0 .. D/2-1."""
+    return np.power(float(base), -2.0 * np.arange(d // 2) / d)
+
+
 def rope(x, pos, base: float = 10000.0, style: int = INTERLEAVED):
     """x [..., L, D] rotated by positions pos [L] (-1 = leave the row unchanged)."""
     x = np.asarray(x, dtype=np.float64)
@@ -41,7 +46,7 @@ def rope(x, pos, base: float = 10000.0, style: int = INTERLEAVED):
     if d % 2:
         raise ValueError("D must be even")
     a, b = rope_pairs(d, style)
-    theta = np.power(float(base), -2.0 * np.arange(d // 2) / d)
+    theta = rope_theta(d, base)
     ang = pos.astype(np.float64)[:, None] * theta[None, :]          # [L, D/2]
     c, s = np.cos(ang), np.sin(ang)
     out = x.copy()

@@ -120,7 +120,10 @@ def call_step(lib, a):
     (dict(q=None), cpr.EINVAL, "q"),
     (dict(q=view(ptr=0)), cpr.EINVAL, "q: data pointer"),
     (dict(k=view(ptr=0x100008)), cpr.EINVAL, "16-byte aligned"),
-    (dict(v=view(sl=100)), cpr.EINVAL, "multiples of 8"),
+    (dict(v=view(sl=132)), cpr.EINVAL, "multiples of 8"),
+    (dict(k=view(sl=64)), cpr.EUNSUPPORTED, "below D"),
+    (dict(q=view(sl=0)), cpr.EUNSUPPORTED, "below D"),
+    (dict(D=64, v=view(sl=56)), cpr.EUNSUPPORTED, "below D"),
     (dict(v=view(sb=-8)), cpr.EINVAL, "negative stride"),
     (dict(q_pos=None), cpr.EINVAL, "position"),
     (dict(kv_pos=None), cpr.EINVAL, "position"),

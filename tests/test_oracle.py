@@ -726,6 +726,79 @@ def test_rope_d2_is_complex_rotation():
     np.testing.assert_allclose(got[..., 1], z.imag, rtol=0, atol=1e-12)
 
 
+# Hand-computed rotation angles pos * theta_j for cases where base^(-2j/D) is exact:
+# (D, base, pos, [angle of pair j = 0 .. D/2-1]). theta_j = base^(-2j/D) gives
+#   D = 8, base = 16:    theta = 1, 1/2, 1/4, 1/8       -> at pos 8:    8, 4, 2, 1
+#   D = 8, base = 10^4:  theta = 1, 0.1, 0.01, 0.001    -> at pos 1000: 1000, 100, 10, 1
+#   D = 4, base = 100:   theta = 1, 0.1                 -> at pos 30:   30, 3
+#   D = 6, base = 64:    theta = 1, 1/4, 1/16           -> at pos 48:   48, 12, 3
+ROPE_HAND_ANGLES = [
+    (8, 16.0, 8, [8.0, 4.0, 2.0, 1.0]),
+    (8, 10000.0, 1000, [1000.0, 100.0, 10.0, 1.0]),
+    (4, 100.0, 30, [30.0, 3.0]),
+    (6, 64.0, 48, [48.0, 12.0, 3.0]),
+]
+# the dimension pairs, written out: INTERLEAVED (2j, 2j+1), HALF (j, j + D/2)
+ROPE_HAND_PAIRS = {
+    (oracle.INTERLEAVED, 8): [(0, 1), (2, 3), (4, 5), (6, 7)],
+    (oracle.HALF, 8): [(0, 4), (1, 5), (2, 6), (3, 7)],
+    (oracle.INTERLEAVED, 4): [(0, 1), (2, 3)],
+    (oracle.HALF, 4): [(0, 2), (1, 3)],
+    (oracle.INTERLEAVED, 6): [(0, 1), (2, 3), (4, 5)],
+    (oracle.HALF, 6): [(0, 3), (1, 4), (2, 5)],
+}
+
+
+@pytest.mark.parametrize("style", [oracle.INTERLEAVED, oracle.HALF])
+@pytest.mark.parametrize("case", range(len(ROPE_HAND_ANGLES)))
+def test_rope_frequency_schedule_hand_computed(style, case):
+    """Every pair j >= 0 turns by the hand-computed angle pos * base^(-2j/D): scalar math.cos / math.sin, one
+    element at a time, on rows at position pos, 0 and a pad (-1)."""
+    d, base, p, angles = ROPE_HAND_ANGLES[case]
+    x = rnd((1, 1, 3, d), 146 + case)
+    got = oracle.rope(x, np.array([p, 0, -1]), base=base, style=style)
+    for (ia, ib), t in zip(ROPE_HAND_PAIRS[(style, d)], angles):
+        a, b = float(x[0, 0, 0, ia]), float(x[0, 0, 0, ib])
+        want_a = a * math.cos(t) - b * math.sin(t)
+        want_b = a * math.sin(t) + b * math.cos(t)
+        assert abs(got[0, 0, 0, ia] - want_a) <= 1e-12 * (1 + abs(want_a)), (ia, t)
+        assert abs(got[0, 0, 0, ib] - want_b) <= 1e-12 * (1 + abs(want_b)), (ib, t)
+    np.testing.assert_array_equal(got[0, 0, 1], x[0, 0, 1])   # position 0
+    np.testing.assert_array_equal(got[0, 0, 2], x[0, 0, 2])   # pad
+
+
+def test_rope_theta_hand_values():
+    """theta_j itself on the hand-computed cases (angle / pos)."""
+    for d, base, p, angles in ROPE_HAND_ANGLES:
+        np.testing.assert_allclose(oracle.rope_theta(d, base), np.array(angles) / p, rtol=1e-15, atol=0)
+
+
+def test_planted_rope_exponent_is_caught(monkeypatch):
+    """theta_j = base^(-j/D) (exponent halved) must fail the hand-computed frequency pin."""
+    import sys
+    rope_mod = sys.modules["oracle.rope"]
+    monkeypatch.setattr(rope_mod, "rope_theta", lambda d, base: np.power(float(base), -1.0 * np.arange(d // 2) / d))
+    for style in (oracle.INTERLEAVED, oracle.HALF):
+        with pytest.raises(AssertionError):
+            test_rope_frequency_schedule_hand_computed(style, 0)
+
+
+def test_planted_rope_pairing_is_caught(monkeypatch):
+    """HALF pairs taken as (j, D - 1 - j) must fail the hand-computed pin."""
+    import sys
+    rope_mod = sys.modules["oracle.rope"]
+    real = rope_mod.rope_pairs
+
+    def wrong(d, style):
+        if style == oracle.HALF:
+            j = np.arange(d // 2)
+            return j, d - 1 - j
+        return real(d, style)
+    monkeypatch.setattr(rope_mod, "rope_pairs", wrong)
+    with pytest.raises(AssertionError):
+        test_rope_frequency_schedule_hand_computed(oracle.HALF, 0)
+
+
 @pytest.mark.parametrize("style", [oracle.INTERLEAVED, oracle.HALF])
 def test_rope_preserves_pair_norms_and_is_identity_at_zero(style):
     x = rnd((2, 3, 9, 16), 141)
