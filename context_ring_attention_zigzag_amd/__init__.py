@@ -31,7 +31,8 @@ OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
 EXPORTS = (
     "cp_padded_len", "cp_zigzag_partition", "cp_shard_gather", "cp_ring_attn_init", "cp_ring_attn_step",
     "cp_ring_attn_merge", "cp_ring_attn_finalize", "cp_ring_attn_workspace_size", "cp_ring_attn_run",
-    "cp_ring_attn_step_ex", "cp_ring_attn_run_ex", "cp_ring_attn_bwd_workspace_size", "cp_ring_attn_bwd_prep",
+    "cp_ring_attn_step_ex", "cp_ring_attn_run_ex", "cp_ring_attn_run_noalloc", "cp_ring_attn_bwd_workspace_size",
+    "cp_ring_attn_bwd_prep",
     "cp_ring_attn_bwd_step", "cp_ring_attn_bwd_run", "cp_rope_apply", "cp_status_string", "cp_last_error",
 )
 
@@ -81,6 +82,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                        vp]),
         "cp_ring_attn_run_ex": (i32, [i32, i32, i32, i32, i32, i32, pv, i32, vp, pv, pv, vp, i32, f32, pe, vp, vp,
                                       vp, ctypes.c_size_t, i32, vp]),
+        "cp_ring_attn_run_noalloc": (i32, [i32, i32, i32, i32, i32, i32, pv, i32, vp, pv, pv, vp, i32, f32, pe, vp,
+                                           vp, vp]),
         "cp_ring_attn_bwd_workspace_size": (ctypes.c_size_t, [i32, i32, i32]),
         "cp_ring_attn_bwd_prep": (i32, [i32, i32, i32, i32, i32, pv, pv, vp, vp, i32, pe, vp, ctypes.c_size_t, vp]),
         "cp_ring_attn_bwd_step": (i32, [i32, i32, i32, i32, i32, pv, pv, i32, pv, pv, i32, vp, f32, vp,
@@ -210,6 +213,25 @@ def cp_ring_attn_run(q_local, q_pos, k_ring, v_ring, ring_pos, cp_size: int, ran
                                       int(bool(causal)), float(softmax_scale), ctypes.byref(ext), _ptr(o_out),
                                       _ptr(lse_out), _ptr(workspace), ws_bytes, flags, _stream(stream)),
            "cp_ring_attn_run_ex")
+
+
+# Bytes of the scratch array cp_ring_attn_run_noalloc keeps on each GPU (CPR_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 34078720
+
+
+def cp_ring_attn_run_noalloc(q_local, q_pos, k_ring, v_ring, ring_pos, cp_size: int, rank: int, causal: bool,
+                             softmax_scale: float, o_out, lse_out=None, stream=None, kw_lo=None, kw_hi=None):
+    """cp_ring_attn_run in fused mode without a workspace: a key split keeps its partial states in the
+    library's scratch array. Allocates nothing (o_out and lse_out are the caller's)."""
+    B, H, Lq, D = q_local.shape
+    qv, kv, vv = view(q_local), view(k_ring), view(v_ring)
+    ext = _ext(q_local, k_ring, kw_lo, kw_hi)
+    _check(load().cp_ring_attn_run_noalloc(dtype_code(q_local), B, H, D, cp_size, rank, ctypes.byref(qv), Lq,
+                                           _ptr(q_pos), ctypes.byref(kv), ctypes.byref(vv), _ptr(ring_pos),
+                                           int(bool(causal)), float(softmax_scale),
+                                           None if ext is None else ctypes.byref(ext), _ptr(o_out), _ptr(lse_out),
+                                           _stream(stream)),
+           "cp_ring_attn_run_noalloc")
 
 
 # ------------------------------------------------------------ backward pass

@@ -2,11 +2,13 @@
 //
 // Every entry point validates all arguments before it touches the HIP
 // runtime, so a bad call returns an error without launching anything. The
-// library holds no state besides the thread-local text of the last error.
+// library holds no state besides the thread-local text of the last error and,
+// for the allocation-free run, each device's address of its scratch array.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "common.h"
@@ -275,11 +277,11 @@ cpr_status cp_ring_attn_run(int32_t dtype, int32_t B, int32_t H, int32_t D, int3
                              softmax_scale, nullptr, o_out, lse_out, workspace, workspace_bytes, flags, stream);
 }
 
-cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t cp_size, int32_t rank,
+// Validation shared by the whole-ring entry points.
+static cpr_status validate_run(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t cp_size, int32_t rank,
                                const cpr_view* q_local, int32_t Lq, const int32_t* q_pos, const cpr_view* k_ring,
-                               const cpr_view* v_ring, const int32_t* ring_pos, int32_t causal, float softmax_scale,
-                               const cpr_attn_ext* ext, void* o_out, float* lse_out, void* workspace,
-                               size_t workspace_bytes, int32_t flags, void* stream) {
+                               const cpr_view* v_ring, const int32_t* ring_pos, float softmax_scale,
+                               const cpr_attn_ext* ext, void* o_out, float* lse_out) {
   if (cp_size < 1) return fail(CPR_EINVAL, "cp_size must be >= 1 (got %d)", cp_size);
   if (rank < 0 || rank >= cp_size) return fail(CPR_EINVAL, "rank %d outside [0, %d)", rank, cp_size);
   TRY(validate_attn(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, (int64_t)Lq * cp_size, ring_pos, ext));
@@ -288,32 +290,47 @@ cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, i
   if (!o_out) return fail(CPR_EINVAL, "o_out is NULL");
   if (!aligned(o_out, 16)) return fail(CPR_EINVAL, "o_out must be 16-byte aligned");
   if (lse_out && !aligned(lse_out, 4)) return fail(CPR_EINVAL, "lse_out must be 4-byte aligned");
+  return CPR_OK;
+}
+
+// Fused whole-ring launch. A grid too small for the chip is split over the
+// keys when `ws` holds the ns partial states (ns = attn_bf16_kv_split);
+// otherwise one launch does everything.
+static cpr_status run_fused(int32_t dtype, AttnArgs a, int32_t cp_size, int32_t rank, void* o_out, float* lse_out,
+                            void* ws, size_t ws_bytes, hipStream_t st) {
+  const size_t rows = (size_t)a.B * a.H * a.Lq;
+  a.nblocks = cp_size; a.rank = rank; a.cp = cp_size;
+  const int32_t ns = dtype == CPR_BF16 ? attn_bf16_kv_split(a.B, a.H, a.Lq, a.Lq) : 1;
+  if (ns > 1 && ws && ws_bytes >= state_bytes(ns, rows, a.D) && aligned(ws, 256)) {
+    char* w = static_cast<char*>(ws);
+    a.o_acc = reinterpret_cast<float*>(w);
+    a.m = reinterpret_cast<float*>(w + round256(ns * rows * a.D * sizeof(float)));
+    a.l = reinterpret_cast<float*>(w + round256(ns * rows * a.D * sizeof(float)) + round256(ns * rows * sizeof(float)));
+    a.kv_split = ns; a.state_rows = (int64_t)rows;
+    a.load_state = 0; a.finalize = 0;
+    const hipError_t e = launch_attn(dtype, a, st);
+    if (e != hipSuccess) return hip_status(e, "cp_ring_attn_run");
+    return hip_status(launch_merge_finalize(1, ns, (int64_t)rows, a.D, a.o_acc, a.m, a.l, o_out, lse_out, st),
+                      "cp_ring_attn_run(merge)");
+  }
+  a.o_out = o_out; a.lse = lse_out;
+  a.load_state = 0; a.finalize = 1;
+  return hip_status(launch_attn(dtype, a, st), "cp_ring_attn_run");
+}
+
+cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t cp_size, int32_t rank,
+                               const cpr_view* q_local, int32_t Lq, const int32_t* q_pos, const cpr_view* k_ring,
+                               const cpr_view* v_ring, const int32_t* ring_pos, int32_t causal, float softmax_scale,
+                               const cpr_attn_ext* ext, void* o_out, float* lse_out, void* workspace,
+                               size_t workspace_bytes, int32_t flags, void* stream) {
+  TRY(validate_run(dtype, B, H, D, cp_size, rank, q_local, Lq, q_pos, k_ring, v_ring, ring_pos, softmax_scale, ext,
+                   o_out, lse_out));
   if (flags != CPR_RUN_FUSED && flags != CPR_RUN_STEPWISE) return fail(CPR_EINVAL, "unknown flags %d", flags);
   const hipStream_t st = static_cast<hipStream_t>(stream);
   AttnArgs a = make_args(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, Lq, ring_pos, causal, softmax_scale,
                          ext);
   const size_t rows = (size_t)B * H * Lq;
-  if (flags == CPR_RUN_FUSED) {
-    a.nblocks = cp_size; a.rank = rank; a.cp = cp_size;
-    // a grid too small for the chip is split over the keys when the caller's
-    // workspace holds the partial states; otherwise one launch does everything
-    const int32_t ns = dtype == CPR_BF16 ? attn_bf16_kv_split(B, H, Lq, Lq) : 1;
-    if (ns > 1 && workspace && workspace_bytes >= state_bytes(ns, rows, D) && aligned(workspace, 256)) {
-      char* w = static_cast<char*>(workspace);
-      a.o_acc = reinterpret_cast<float*>(w);
-      a.m = reinterpret_cast<float*>(w + round256(ns * rows * D * sizeof(float)));
-      a.l = reinterpret_cast<float*>(w + round256(ns * rows * D * sizeof(float)) + round256(ns * rows * sizeof(float)));
-      a.kv_split = ns; a.state_rows = (int64_t)rows;
-      a.load_state = 0; a.finalize = 0;
-      const hipError_t e = launch_attn(dtype, a, st);
-      if (e != hipSuccess) return hip_status(e, "cp_ring_attn_run");
-      return hip_status(launch_merge_finalize(1, ns, (int64_t)rows, D, a.o_acc, a.m, a.l, o_out, lse_out, st),
-                        "cp_ring_attn_run(merge)");
-    }
-    a.o_out = o_out; a.lse = lse_out;
-    a.load_state = 0; a.finalize = 1;
-    return hip_status(launch_attn(dtype, a, st), "cp_ring_attn_run");
-  }
+  if (flags == CPR_RUN_FUSED) return run_fused(dtype, a, cp_size, rank, o_out, lse_out, workspace, workspace_bytes, st);
   const size_t need = state_bytes(1, rows, D);
   if (!workspace || workspace_bytes < need)
     return fail(CPR_EINVAL, "stepwise run needs a workspace of %zu bytes", need);
@@ -333,6 +350,75 @@ cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, i
   }
   return hip_status(launch_finalize(dtype == CPR_BF16, (int64_t)rows, D, o_acc, m, l, o_out, lse_out, st),
                     "cp_ring_attn_run(finalize)");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------ allocation-free fused run
+//
+// The partial states of a key-split fused run live in `scratch`, one copy per
+// GPU, held from the library's load until the process ends. Size bound: the
+// split happens only when the unsplit grid g = ceil(Lq / 256) * B * H has
+// 2g <= 256 workgroups, into ns <= 256 / g slices, so the partial states cover
+// ns * B * H * Lq <= ns * g * 256 <= 65,536 rows: at D = 128, 65,536 float32
+// rows of O plus the m and l planes, each plane 256-byte aligned.
+namespace {
+constexpr size_t kScratchRows = 65536;
+constexpr size_t kScratchBytes = CPR_NOALLOC_SCRATCH_BYTES;
+static_assert(kScratchBytes == kScratchRows * 128 * sizeof(float) + 2 * kScratchRows * sizeof(float),
+              "65,536 rows of the D = 128 state");
+static_assert(kScratchBytes % 256 == 0 && (kScratchRows * 128 * sizeof(float)) % 256 == 0,
+              "planes stay 256-byte aligned");
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` on each device, once looked up
+
+// The current device's copy of `scratch`: its address is looked up once per
+// device with that device current; host code then uses only that address.
+cpr_status current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CPR_EUNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256)) return fail(CPR_EHIP, "scratch address %p is not 256-byte aligned", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CPR_OK;
+}
+}  // namespace
+
+extern "C" {
+
+cpr_status cp_ring_attn_run_noalloc(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t cp_size, int32_t rank,
+                                    const cpr_view* q_local, int32_t Lq, const int32_t* q_pos,
+                                    const cpr_view* k_ring, const cpr_view* v_ring, const int32_t* ring_pos,
+                                    int32_t causal, float softmax_scale, const cpr_attn_ext* ext, void* o_out,
+                                    float* lse_out, void* stream) {
+  TRY(validate_run(dtype, B, H, D, cp_size, rank, q_local, Lq, q_pos, k_ring, v_ring, ring_pos, softmax_scale, ext,
+                   o_out, lse_out));
+  void* ws = nullptr;
+  TRY(current_scratch(&ws));
+  const size_t rows = (size_t)B * H * Lq;
+  const int32_t ns = dtype == CPR_BF16 ? attn_bf16_kv_split(B, H, Lq, Lq) : 1;
+  const size_t need = ns > 1 ? state_bytes(ns, rows, D) : 0;
+  if (need > kScratchBytes)
+    return fail(CPR_EUNSUPPORTED, "key-split partial states need %zu bytes, above the %zu-byte scratch", need,
+                kScratchBytes);
+  AttnArgs a = make_args(dtype, B, H, D, q_local, Lq, q_pos, k_ring, v_ring, Lq, ring_pos, causal, softmax_scale,
+                         ext);
+  return run_fused(dtype, a, cp_size, rank, o_out, lse_out, ns > 1 ? ws : nullptr, need,
+                   static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------- backward

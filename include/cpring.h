@@ -28,7 +28,8 @@
  *  - Every pointer argument named as device memory must point to memory of
  *    the current HIP device; position arrays are int32 device arrays.
  *  - The caller owns every buffer. The library never allocates or frees
- *    device memory and keeps no state between calls.
+ *    device memory and keeps no state between calls, apart from the static
+ *    scratch array of cp_ring_attn_run_noalloc (loaded with the library).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and does not synchronise. Results are valid once the stream has
  *    reached the call.
@@ -257,6 +258,34 @@ cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D,
                                int32_t causal, float softmax_scale, const cpr_attn_ext* ext,
                                void* o_out, float* lse_out,
                                void* workspace, size_t workspace_bytes, int32_t flags, void* stream);
+
+/*
+ * cp_ring_attn_run_ex in CPR_RUN_FUSED mode, for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation). Arguments, results and
+ * errors are those of cp_ring_attn_run_ex with flags = CPR_RUN_FUSED; there is
+ * no workspace argument. When the grid is too small for the GPU, the per-slice
+ * partial states of the key split go to a scratch array inside the library
+ * (CPR_NOALLOC_SCRATCH_BYTES per GPU, held from the library's load until the
+ * process ends) instead of a caller's workspace; the split, and so the result,
+ * is the same as cp_ring_attn_run's with a workspace of
+ * cp_ring_attn_workspace_size() bytes. A split whose partial states would not
+ * fit returns CPR_EUNSUPPORTED (the split rule keeps them within 65,536 rows,
+ * so this does not happen for any valid shape). The call allocates nothing:
+ * the scratch address is looked up on the call's first use of a device.
+ * Every call on one GPU shares that GPU's scratch and leaves its contents
+ * behind: calls that overlap in time on one GPU (two streams, two threads)
+ * race and must be ordered by the caller. Each split launch writes every
+ * partial row it later reads, so no clearing is needed between calls.
+ */
+#define CPR_NOALLOC_SCRATCH_BYTES ((size_t)34078720) /* 65,536 rows x (128 + 2) floats */
+
+cpr_status cp_ring_attn_run_noalloc(int32_t dtype, int32_t B, int32_t H, int32_t D,
+                                    int32_t cp_size, int32_t rank,
+                                    const cpr_view* q_local, int32_t Lq, const int32_t* q_pos,
+                                    const cpr_view* k_ring, const cpr_view* v_ring, const int32_t* ring_pos,
+                                    int32_t causal, float softmax_scale, const cpr_attn_ext* ext,
+                                    void* o_out, float* lse_out, void* stream);
 
 /*
  * Backward pass: the gradients of one rank's attention output (the glossary
