@@ -231,7 +231,10 @@ def bench_backward(args, cpr, di, torch, np, w, gen_slice, lay_codes):
     dq = torch.empty(ri.q_local.shape, dtype=torch.float32, device="cuda")
     dk = torch.empty(ri.k_ring.shape, dtype=torch.float32, device="cuda")
     dv = torch.empty(ri.v_ring.shape, dtype=torch.float32, device="cuda")
-    ws = torch.empty(cpr.cp_ring_attn_bwd_workspace_size(w.B, w.H, ri.lq), dtype=torch.uint8, device="cuda")
+    # sized for the split of a grid too small for the GPU (equals the base size for large grids)
+    ws_bytes = cpr.cp_ring_attn_bwd_workspace_size_ex(w.B, w.H, w.H, w.D, ri.lq, w.cp * ri.lq)
+    split = ws_bytes > cpr.cp_ring_attn_bwd_workspace_size(w.B, w.H, ri.lq)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     pairs = allowed_pairs(w, ri.s_pad, ri.lq, ri.q_pos.cpu().numpy(), ri.ring_pos.cpu().numpy())
     # FlashAttention convention: the backward is 2.5 forward passes (S recomputed, dP, dV, dQ, dK)
@@ -263,10 +266,12 @@ def bench_backward(args, cpr, di, torch, np, w, gen_slice, lay_codes):
         "pct_of_peak": round(100.0 * value / peak, 2),
         "config": {"workload": w.name, "pass": "backward", "B": w.B, "H": w.H, "D": w.D, "seq_len": w.S,
                    "cp_size": w.cp, "layout": w.layout, "rank": rank, "causal": w.causal, "local_queries": ri.lq,
-                   "allowed_pairs_per_bh": pairs},
+                   "allowed_pairs_per_bh": pairs, "small_grid_split": bool(split)},
         "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": round(value, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(value / peak, 4), "traffic": None,
-                     "kernel": "bwd_prep + bwd_dq_kernel + bwd_dkv_kernel (one call)", "kernel_ms": round(ms, 4),
+                     "kernel": "bwd_prep + bwd_dq_kernel + bwd_dkv_kernel" + (" (split) + bwd_reduce_kernel"
+                                                                             if split else "") + " (one call)",
+                     "kernel_ms": round(ms, 4),
                      "flop_per_launch": flop},
     }
     print(json.dumps(line), flush=True)

@@ -32,7 +32,7 @@ EXPORTS = (
     "cp_padded_len", "cp_zigzag_partition", "cp_shard_gather", "cp_ring_attn_init", "cp_ring_attn_step",
     "cp_ring_attn_merge", "cp_ring_attn_finalize", "cp_ring_attn_workspace_size", "cp_ring_attn_run",
     "cp_ring_attn_step_ex", "cp_ring_attn_run_ex", "cp_ring_attn_run_noalloc", "cp_ring_attn_bwd_workspace_size",
-    "cp_ring_attn_bwd_prep",
+    "cp_ring_attn_bwd_workspace_size_ex", "cp_ring_attn_bwd_prep",
     "cp_ring_attn_bwd_step", "cp_ring_attn_bwd_run", "cp_rope_apply", "cp_status_string", "cp_last_error",
 )
 
@@ -85,6 +85,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "cp_ring_attn_run_noalloc": (i32, [i32, i32, i32, i32, i32, i32, pv, i32, vp, pv, pv, vp, i32, f32, pe, vp,
                                            vp, vp]),
         "cp_ring_attn_bwd_workspace_size": (ctypes.c_size_t, [i32, i32, i32]),
+        "cp_ring_attn_bwd_workspace_size_ex": (ctypes.c_size_t, [i32, i32, i32, i32, i32, i64]),
         "cp_ring_attn_bwd_prep": (i32, [i32, i32, i32, i32, i32, pv, pv, vp, vp, i32, pe, vp, ctypes.c_size_t, vp]),
         "cp_ring_attn_bwd_step": (i32, [i32, i32, i32, i32, i32, pv, pv, i32, pv, pv, i32, vp, f32, vp,
                                         ctypes.c_size_t, vp, vp, vp, vp]),
@@ -248,6 +249,11 @@ def _win_ext(h_kv: int, kw_lo, kw_hi):
 
 def cp_ring_attn_bwd_workspace_size(B: int, H: int, Lq: int) -> int:
     return load().cp_ring_attn_bwd_workspace_size(B, H, Lq)
+
+
+def cp_ring_attn_bwd_workspace_size_ex(B: int, H: int, H_kv: int, D: int, Lq: int, Lk: int) -> int:
+    """Workspace bytes with room for the split of a small backward grid (Lk: K/V rows of the call)."""
+    return load().cp_ring_attn_bwd_workspace_size_ex(B, H, H_kv, D, Lq, Lk)
 
 
 def cp_ring_attn_bwd_prep(o, do, lse, q_pos, causal: bool, workspace, kw_lo=None, kw_hi=None, stream=None):

@@ -428,6 +428,51 @@ size_t cp_ring_attn_bwd_workspace_size(int32_t B, int32_t H, int32_t Lq) {
   return 2 * round256((size_t)B * H * Lq * 4) + round256((size_t)Lq * 8);
 }
 
+// Bytes of the partial gradients a split backward launch keeps after the
+// preprocessing planes (0 when neither kernel splits): dQ partials of
+// q_split slices, then dK and dV partials of kv_split slices, each plane
+// 256-byte aligned.
+static size_t bwd_split_bytes(int32_t B, int32_t H, int32_t H_kv, int32_t D, int32_t Lq, int64_t Lk_total,
+                              int32_t* q_split, int32_t* kv_split) {
+  const int32_t nq = bwd_bf16_q_split(B, H, Lq);
+  const int32_t nk = bwd_bf16_kv_split(B, H_kv, Lk_total);
+  if (q_split) *q_split = nq;
+  if (kv_split) *kv_split = nk;
+  size_t bytes = 0;
+  if (nq > 1) bytes += round256((size_t)nq * B * H * Lq * D * sizeof(float));
+  if (nk > 1) bytes += 2 * round256((size_t)nk * B * H_kv * (size_t)Lk_total * D * sizeof(float));
+  return bytes;
+}
+
+size_t cp_ring_attn_bwd_workspace_size_ex(int32_t B, int32_t H, int32_t H_kv, int32_t D, int32_t Lq, int64_t Lk) {
+  const size_t base = cp_ring_attn_bwd_workspace_size(B, H, Lq);
+  if (!base || (D != 64 && D != 128) || H_kv < 0 || (H_kv > 0 && H % H_kv) || Lk < 1 || Lk > CPR_MAX_SEQ) return 0;
+  return base + bwd_split_bytes(B, H, H_kv > 0 ? H_kv : H, D, Lq, Lk, nullptr, nullptr);
+}
+
+// Engage the split of a bf16 backward launch when the workspace holds the
+// partial gradients; otherwise leave it unsplit.
+static void bwd_plan_split(int32_t dtype, BwdArgs& a, int64_t Lk_total, void* ws, size_t bytes) {
+  a.q_split = a.kv_split = 1;
+  if (dtype != CPR_BF16) return;
+  int32_t nq, nk;
+  const size_t extra = bwd_split_bytes(a.B, a.H, a.H_kv, a.D, a.Lq, Lk_total, &nq, &nk);
+  const size_t base = cp_ring_attn_bwd_workspace_size(a.B, a.H, a.Lq);
+  if (!extra || bytes < base + extra) return;
+  char* w = static_cast<char*>(ws) + base;
+  if (nq > 1) {
+    a.q_split = nq;
+    a.dq_part = reinterpret_cast<float*>(w);
+    w += round256((size_t)nq * a.B * a.H * a.Lq * a.D * sizeof(float));
+  }
+  if (nk > 1) {
+    const size_t plane = round256((size_t)nk * a.B * a.H_kv * (size_t)Lk_total * a.D * sizeof(float));
+    a.kv_split = nk;
+    a.dk_part = reinterpret_cast<float*>(w);
+    a.dv_part = reinterpret_cast<float*>(w + plane);
+  }
+}
+
 static cpr_status check_bwd_workspace(int32_t B, int32_t H, int32_t Lq, const void* ws, size_t bytes) {
   const size_t need = cp_ring_attn_bwd_workspace_size(B, H, Lq);
   if (!ws || bytes < need) return fail(CPR_EINVAL, "backward workspace needs %zu bytes", need);
@@ -528,6 +573,7 @@ cpr_status cp_ring_attn_bwd_step(int32_t dtype, int32_t B, int32_t H, int32_t D,
   a.nblocks = 1; a.rank = 0; a.cp = 1;
   a.dq = dq_acc; a.dk = dk_acc; a.dv = dv_acc;
   a.accumulate = 1;
+  bwd_plan_split(dtype, a, Lk, const_cast<void*>(workspace), workspace_bytes);
   return hip_status(launch_bwd(dtype, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_bwd_step");
 }
 
@@ -557,6 +603,7 @@ cpr_status cp_ring_attn_bwd_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
   a.nblocks = cp_size; a.rank = rank; a.cp = cp_size;
   a.dq = dq_local; a.dk = dk_ring; a.dv = dv_ring;
   a.accumulate = 0;
+  bwd_plan_split(dtype, a, (int64_t)Lq * cp_size, workspace, workspace_bytes);
   return hip_status(launch_bwd(dtype, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_bwd_run");
 }
 

@@ -259,7 +259,7 @@ constexpr int kQThreads = 64 * kQWaves;
 constexpr int kQOwn = 32 * kQWaves;           // queries per workgroup
 constexpr int kQMaxTiles = 8 * kQThreads;     // key tiles classified per segment
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
   using C = BCfg<D>;
   constexpr int kLoads = C::kTileLoads / kQWaves;   // per wave per tensor
@@ -280,7 +280,12 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
   const int hh = lane >> 5;
 
   const int nqt = (a.Lq + kQOwn - 1) / kQOwn;
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  int logical = xcd_logical(blockIdx.x, gridDim.x);
+  int slice = 0;   // key slice of a split launch; the slices of one query tile are adjacent
+  if constexpr (SPLIT) {
+    slice = logical % a.q_split;
+    logical /= a.q_split;
+  }
   const int bh = logical / nqt;
   const int qt = nqt - 1 - (logical - bh * nqt);
   const int b = bh / a.H;
@@ -354,6 +359,12 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
   const __bf16* kbh = static_cast<const __bf16*>(a.k) + b * a.k_sb + hk * a.k_sh;
   const __bf16* vbh = static_cast<const __bf16*>(a.v) + b * a.v_sb + hk * a.v_sh;
   const int n_kt = (a.Lk + kT - 1) / kT;
+  // key tiles of every block that this workgroup walks: all, or its slice
+  int kt_lo = 0, kt_hi = n_kt;
+  if constexpr (SPLIT) {
+    kt_lo = (int)((int64_t)slice * n_kt / a.q_split);
+    kt_hi = (int)((int64_t)(slice + 1) * n_kt / a.q_split);
+  }
   // this wave's share of a tile: LDS chunk slots (wave * kLoads + i) * 64 + lane
   uint32_t k_off[kLoads], v_off[kLoads];
 #pragma unroll
@@ -375,8 +386,8 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
     const __bf16* kb = kbh + row0 * a.k_sl;
     const __bf16* vb = vbh + row0 * a.v_sl;
 
-    for (int seg0 = 0; seg0 < n_kt; seg0 += kQMaxTiles) {
-      const int nseg = min(kQMaxTiles, n_kt - seg0);
+    for (int seg0 = kt_lo; seg0 < kt_hi; seg0 += kQMaxTiles) {
+      const int nseg = min(kQMaxTiles, kt_hi - seg0);
       // ---- classify the segment's key tiles: 8 lanes per tile, 4 positions each
       bar();
       for (int base = 0; base < nseg; base += kQThreads / 8) {
@@ -486,7 +497,8 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
   }
 
   if (!q_in) return;
-  float* out = a.dq + srow * D;
+  // a split launch writes its slice's partial dQ
+  float* out = SPLIT ? a.dq_part + ((int64_t)slice * a.B * a.H * a.Lq + srow) * D : a.dq + srow * D;
 #pragma unroll
   for (int dt = 0; dt < C::kDTiles; ++dt)
 #pragma unroll
@@ -494,7 +506,7 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
       float4 x = make_float4(a.scale * dqt[dt][4 * i + 0], a.scale * dqt[dt][4 * i + 1], a.scale * dqt[dt][4 * i + 2],
                              a.scale * dqt[dt][4 * i + 3]);
       float4* p = reinterpret_cast<float4*>(out + 32 * dt + 8 * i + 4 * hh);
-      if (a.accumulate) {
+      if (!SPLIT && a.accumulate) {
         const float4 y = *p;
         x.x += y.x;
         x.y += y.y;
@@ -526,7 +538,7 @@ constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvOwn = 128;                   // keys per workgroup, 32 per pair
 constexpr int kKvMaxTiles = 8 * kKvThreads;   // query tiles classified per segment
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
   using C = BCfg<D>;
   constexpr int kTileElems = kT * D;   // elements of one streamed tile buffer
@@ -554,7 +566,12 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
 
   const int64_t lk_total = (int64_t)a.nblocks * a.Lk;
   const int nkt = (int)((lk_total + kKvOwn - 1) / kKvOwn);
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  int logical = xcd_logical(blockIdx.x, gridDim.x);
+  int slice = 0;   // query slice of a split launch; the slices of one key tile are adjacent
+  if constexpr (SPLIT) {
+    slice = logical % a.kv_split;
+    logical /= a.kv_split;
+  }
   const int bhk = logical / nkt;
   const int kt = logical - bhk * nkt;
   const int b = bhk / a.H_kv;
@@ -607,6 +624,12 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
   const float c2 = a.scale * kLog2e;
   const int group = a.H / a.H_kv;
   const int n_qt = (a.Lq + kT - 1) / kT;
+  // query tiles this workgroup walks: all, or its slice
+  int qt_lo = 0, qt_hi = n_qt;
+  if constexpr (SPLIT) {
+    qt_lo = (int)((int64_t)slice * n_qt / a.kv_split);
+    qt_hi = (int)((int64_t)(slice + 1) * n_qt / a.kv_split);
+  }
   // role A's share of an item's loads: Q (waves 0, 1) or dO (waves 2, 3), LDS
   // chunk slots ((wave & 1) * kLoads + i) * 64 + lane
   const bool load_q = wave < 2;
@@ -624,8 +647,8 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
   // the other's are live; both copies pass the same sequence of barriers.
   auto run = [&](auto role) __attribute__((always_inline)) {
     constexpr bool kA = decltype(role)::value;
-    for (int seg0 = 0; seg0 < n_qt && kmax >= 0; seg0 += kKvMaxTiles) {
-      const int nseg = min(kKvMaxTiles, n_qt - seg0);
+    for (int seg0 = qt_lo; seg0 < qt_hi && kmax >= 0; seg0 += kKvMaxTiles) {
+      const int nseg = min(kKvMaxTiles, qt_hi - seg0);
       // ---- classify the segment's query tiles: 8 lanes per tile, 4 queries each
       bar();
       for (int base = 0; base < nseg; base += kKvThreads / 8) {
@@ -877,7 +900,9 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
 
     if (!k_in) return;
     const int64_t krow = (int64_t)bhk * lk_total + k_idx;
-    float* out = (kA ? a.dv : a.dk) + krow * D;
+    // a split launch writes its slice's partial dK / dV
+    float* out = SPLIT ? (kA ? a.dv_part : a.dk_part) + ((int64_t)slice * a.B * a.H_kv * lk_total + krow) * D
+                       : (kA ? a.dv : a.dk) + krow * D;
     const float sc = kA ? 1.f : a.scale;
   #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
@@ -886,7 +911,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
         float4 x = make_float4(sc * acc[dt][4 * i + 0], sc * acc[dt][4 * i + 1], sc * acc[dt][4 * i + 2],
                                sc * acc[dt][4 * i + 3]);
         float4* p = reinterpret_cast<float4*>(out + 32 * dt + 8 * i + 4 * hh);
-        if (a.accumulate) {
+        if (!SPLIT && a.accumulate) {
           const float4 y = *p;
           x.x += y.x;
           x.y += y.y;
@@ -901,21 +926,88 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
   else run(std::false_type{});
 }
 
+// Sum of the partial gradients of a split launch, in slice order:
+// out[i] = (accumulate ? out[i] : 0) + part[0][i] + part[1][i] + ...
+// blockIdx.y picks one of up to three (partials, output) pairs.
+struct ReduceArgs {
+  const float4* part[3];
+  float4* out[3];
+  int64_t n4[3];     // float4 elements of one output
+  int32_t ns[3];     // slices
+  int32_t accumulate;
+};
+
+__global__ void __launch_bounds__(256) bwd_reduce_kernel(ReduceArgs r) {
+  const int y = blockIdx.y;
+  const int64_t n4 = r.n4[y];
+  const float4* part = r.part[y];
+  float4* out = r.out[y];
+  const int ns = r.ns[y];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    float4 s = r.accumulate ? out[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < ns; ++j) {
+      const float4 x = part[(int64_t)j * n4 + i];
+      s.x += x.x;
+      s.y += x.y;
+      s.z += x.z;
+      s.w += x.w;
+    }
+    out[i] = s;
+  }
+}
+
 template <int D>
 hipError_t launch_bwd(const BwdArgs& a, int32_t do_dq, int32_t do_dkv, hipStream_t st) {
+  const bool qs = do_dq && a.q_split > 1, ks = do_dkv && a.kv_split > 1;
   if (do_dq) {
     const int nqt = (a.Lq + kQOwn - 1) / kQOwn;
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3((unsigned)(nqt * a.B * a.H)), dim3(kQThreads), 0, st, a);
+    if (qs)
+      hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3((unsigned)(nqt * a.B * a.H * a.q_split)), dim3(kQThreads), 0,
+                         st, a);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3((unsigned)(nqt * a.B * a.H)), dim3(kQThreads), 0, st, a);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const int64_t lk_total = (int64_t)a.nblocks * a.Lk;
   if (do_dkv) {
-    const int64_t lk_total = (int64_t)a.nblocks * a.Lk;
     const int64_t nkt = (lk_total + kKvOwn - 1) / kKvOwn;
-    hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3((unsigned)(nkt * a.B * a.H_kv)), dim3(kKvThreads), 0, st, a);
-    return hipGetLastError();
+    if (ks)
+      hipLaunchKernelGGL((bwd_dkv_kernel<D, true>), dim3((unsigned)(nkt * a.B * a.H_kv * a.kv_split)),
+                         dim3(kKvThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL((bwd_dkv_kernel<D, false>), dim3((unsigned)(nkt * a.B * a.H_kv)), dim3(kKvThreads), 0, st,
+                         a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  if (!qs && !ks) return hipSuccess;
+  ReduceArgs r{};
+  int n = 0;
+  if (qs) {
+    r.part[n] = reinterpret_cast<const float4*>(a.dq_part);
+    r.out[n] = reinterpret_cast<float4*>(a.dq);
+    r.n4[n] = (int64_t)a.B * a.H * a.Lq * D / 4;
+    r.ns[n++] = a.q_split;
+  }
+  if (ks) {
+    const int64_t n4 = (int64_t)a.B * a.H_kv * lk_total * D / 4;
+    r.part[n] = reinterpret_cast<const float4*>(a.dk_part);
+    r.out[n] = reinterpret_cast<float4*>(a.dk);
+    r.n4[n] = n4;
+    r.ns[n++] = a.kv_split;
+    r.part[n] = reinterpret_cast<const float4*>(a.dv_part);
+    r.out[n] = reinterpret_cast<float4*>(a.dv);
+    r.n4[n] = n4;
+    r.ns[n++] = a.kv_split;
+  }
+  r.accumulate = a.accumulate;
+  int64_t most = 0;
+  for (int i = 0; i < n; ++i) most = r.n4[i] > most ? r.n4[i] : most;
+  const int64_t blocks = (most + 255) / 256;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)(blocks < 1024 ? blocks : 1024), (unsigned)n), dim3(256), 0,
+                     st, r);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
@@ -928,6 +1020,25 @@ hipError_t launch_prep_t(const BwdPrepArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+// Split only grids that fill at most half of the workgroup slots (the dQ
+// kernel runs two workgroups per compute unit, the dK/dV kernel one), into as
+// many slices as bring them to about one full round, at most 16.
+int32_t bwd_bf16_q_split(int32_t B, int32_t H, int32_t Lq) {
+  constexpr int64_t kSlots = 2 * 256, kMaxSplit = 16;
+  if (B < 1 || H < 1 || Lq < 1) return 1;
+  const int64_t grid = (int64_t)((Lq + kQOwn - 1) / kQOwn) * B * H;
+  if (2 * grid > kSlots) return 1;
+  return (int32_t)(kSlots / grid < kMaxSplit ? kSlots / grid : kMaxSplit);
+}
+
+int32_t bwd_bf16_kv_split(int32_t B, int32_t H_kv, int64_t Lk_total) {
+  constexpr int64_t kSlots = 256, kMaxSplit = 16;
+  if (B < 1 || H_kv < 1 || Lk_total < 1) return 1;
+  const int64_t grid = (Lk_total + kKvOwn - 1) / kKvOwn * B * H_kv;
+  if (2 * grid > kSlots) return 1;
+  return (int32_t)(kSlots / grid < kMaxSplit ? kSlots / grid : kMaxSplit);
+}
 
 hipError_t launch_bwd_prep(int32_t dtype_bf16, const BwdPrepArgs& a, hipStream_t st) {
   if (dtype_bf16) return a.D == 64 ? launch_prep_t<__bf16, 64>(a, st) : launch_prep_t<__bf16, 128>(a, st);

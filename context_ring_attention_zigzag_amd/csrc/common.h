@@ -90,7 +90,21 @@ struct BwdArgs {
   float scale;
   float* dq; float* dk; float* dv;
   int32_t accumulate;
+  // split for grids too small for the GPU (bf16 path): q_split > 1 gives each
+  // dQ query tile q_split workgroups, slice j covering key tiles
+  // [j * n / q_split, (j + 1) * n / q_split) of every block (n = key tiles per
+  // block) and writing its partial dQ to dq_part + j * B*H*Lq*D; kv_split > 1
+  // likewise splits the query tiles of each dK/dV key tile, partials at
+  // dk_part / dv_part + j * B*H_kv*nblocks*Lk*D. launch_bwd_bf16 then sums the
+  // partials in slice order into dq / dk / dv (added to them when accumulate).
+  int32_t q_split, kv_split;
+  float* dq_part; float* dk_part; float* dv_part;
 };
+
+// Slices of the backward split (BwdArgs::q_split, kv_split) for a bf16 pass:
+// > 1 when the unsplit grid would leave most of the chip idle, else 1.
+int32_t bwd_bf16_q_split(int32_t B, int32_t H, int32_t Lq);
+int32_t bwd_bf16_kv_split(int32_t B, int32_t H_kv, int64_t Lk_total);
 
 hipError_t launch_bwd_prep(int32_t dtype_bf16, const BwdPrepArgs& a, hipStream_t st);
 hipError_t launch_bwd_bf16(const BwdArgs& a, int32_t do_dq, int32_t do_dkv, hipStream_t st);

@@ -312,6 +312,24 @@ cpr_status cp_ring_attn_run_noalloc(int32_t dtype, int32_t B, int32_t H, int32_t
  * key-position window per query. Returns 0 for invalid sizes. */
 size_t cp_ring_attn_bwd_workspace_size(int32_t B, int32_t H, int32_t Lq);
 
+/* Workspace bytes that also let a bf16 backward call on a grid too small for
+ * the GPU split its work: the dQ kernel over the keys of each block, the
+ * dK/dV kernel over the queries, each slice writing float32 partial
+ * gradients that a reduction pass then sums in slice order (deterministic:
+ * no atomics). This is the partial-sum counterpart of the forward's key split
+ * (the running-max rule of "Sequence Parallelism and Ring Attention",
+ * "Technical insight", is not needed here: gradients simply add up over
+ * disjoint key or query sets), sized for the glossary page's small example
+ * ("Context Parallelism", "Practical use and trade-offs": 1 x 4 x 4096 x 64
+ * on two ranks, differentiated). H_kv = 0 means H; Lk is the number of K/V
+ * rows the call covers: cp_size * Lq for cp_ring_attn_bwd_run, the block's
+ * Lk for cp_ring_attn_bwd_step. Equals cp_ring_attn_bwd_workspace_size(B, H,
+ * Lq) when the grids are large enough not to split. Returns 0 for invalid
+ * sizes. A call given at least this many bytes splits; given fewer (but at
+ * least the base size) it runs unsplit. Only the float32 summation order
+ * changes. */
+size_t cp_ring_attn_bwd_workspace_size_ex(int32_t B, int32_t H, int32_t H_kv, int32_t D, int32_t Lq, int64_t Lk);
+
 /*
  * Backward preprocessing of one rank's queries, once per backward pass. Fills
  * `workspace` (cp_ring_attn_bwd_workspace_size(B, H, Lq) bytes, 256-byte
@@ -332,7 +350,10 @@ cpr_status cp_ring_attn_bwd_prep(int32_t dtype, int32_t B, int32_t H, int32_t D,
  *   q, dout    [B,H,Lq,D] views of dtype: local queries and dO;
  *   k, v       [B,H_kv,Lk,D] views of dtype: the block (H_kv = 0 means H),
  *              positions kv_pos [Lk];
- *   workspace  filled by cp_ring_attn_bwd_prep for these queries;
+ *   workspace  filled by cp_ring_attn_bwd_prep for these queries; with
+ *              cp_ring_attn_bwd_workspace_size_ex(B, H, H_kv, D, Lq, Lk)
+ *              bytes a small grid splits, using the bytes past the
+ *              preprocessing planes as scratch;
  *   dq_acc     [B,H,Lq,D] float32: dq_acc += scale * dS k;
  *   dk_acc, dv_acc  [B,H_kv,Lk,D] float32: += the rank's share of the
  *              block's dK and dV (the buffers that travel with the block).
@@ -354,7 +375,11 @@ cpr_status cp_ring_attn_bwd_step(int32_t dtype, int32_t B, int32_t H, int32_t D,
  *   dk_ring, dv_ring  [B,H_kv,cp_size*Lq,D] float32, written, in ring order
  *              like k_ring: summed over all ranks they are the full
  *              gradients of K and V;
- *   workspace  cp_ring_attn_bwd_workspace_size(B, H, Lq) bytes, 256-byte aligned.
+ *   workspace  cp_ring_attn_bwd_workspace_size(B, H, Lq) bytes, 256-byte
+ *              aligned, or cp_ring_attn_bwd_workspace_size_ex(B, H, H_kv, D,
+ *              Lq, cp_size * Lq) bytes to let a small grid split.
+ * The workspace is scratch that the call overwrites: calls in flight at the
+ * same time must not share one.
  */
 cpr_status cp_ring_attn_bwd_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
                                 int32_t cp_size, int32_t rank,

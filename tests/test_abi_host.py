@@ -293,3 +293,16 @@ def test_rope_validation(lib):
     assert call(out=fake_ptr(0x100008)) == cpr.EINVAL and "16-byte" in err(lib)
     assert call(D=80) == cpr.EUNSUPPORTED
     assert call(dtype=cpr.F32, xv=view(sl=130)) == cpr.EINVAL
+
+
+def test_bwd_workspace_size_ex(lib):
+    base = lib.cp_ring_attn_bwd_workspace_size
+    ex = lib.cp_ring_attn_bwd_workspace_size_ex
+    # the glossary example's rank: small grids, room for partial gradients
+    assert ex(1, 4, 4, 64, 2048, 4096) > base(1, 4, 2048)
+    assert ex(1, 4, 0, 64, 2048, 4096) == ex(1, 4, 4, 64, 2048, 4096)
+    # the non-causal 65,536-token share: large grids, no split
+    assert ex(2, 16, 16, 128, 8192, 65536) == base(2, 16, 8192)
+    for bad in ((0, 4, 4, 64, 2048, 4096), (1, 4, 3, 64, 2048, 4096), (1, 4, 4, 96, 2048, 4096),
+                (1, 4, 4, 64, 0, 4096), (1, 4, 4, 64, 2048, 0), (1, 4, -1, 64, 2048, 4096)):
+        assert ex(*bad) == 0, bad

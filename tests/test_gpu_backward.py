@@ -111,12 +111,16 @@ class Case:
         self.zero_rows = (~ok.any(axis=1), ~ok.any(axis=0), ~ok.any(axis=0))   # dQ, dK, dV
         return ri, do_local, o_dev, lse_dev, kw, ref
 
-    def run_gpu(self, r, ri, do_local, o_dev, lse_dev, kw):
+    def run_gpu(self, r, ri, do_local, o_dev, lse_dev, kw, split=False, ws_bytes=None):
+        """split: pass the workspace that lets a small grid split (cp_ring_attn_bwd_workspace_size_ex)."""
         dq = torch.full(ri.q_local.shape, float("nan"), dtype=torch.float32, device="cuda")
         dk = torch.full(ri.k_ring.shape, float("nan"), dtype=torch.float32, device="cuda")
         dv = torch.full(ri.v_ring.shape, float("nan"), dtype=torch.float32, device="cuda")
-        ws = torch.empty(cpr.cp_ring_attn_bwd_workspace_size(self.B, self.H, self.lq), dtype=torch.uint8,
-                         device="cuda")
+        if ws_bytes is None:
+            ws_bytes = (cpr.cp_ring_attn_bwd_workspace_size_ex(self.B, self.H, self.H_kv, self.D, self.lq,
+                                                               self.cp * self.lq) if split else
+                        cpr.cp_ring_attn_bwd_workspace_size(self.B, self.H, self.lq))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
         cpr.cp_ring_attn_bwd_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, self.cp, r, o_dev,
                                  do_local, lse_dev, self.causal, 0.0, dq, dk, dv, ws, **kw)
         torch.cuda.synchronize()
@@ -310,6 +314,81 @@ def test_bwd_full_size_sampled(wl_name):
         got_v = dv[b, h0, torch.from_numpy(k_rows).cuda()].cpu().numpy()
         for g, r, n in ((got_q, ref_q, "dQ"), (got_k, ref_k, "dK"), (got_v, ref_v, "dV")):
             check(g, r, "bf16", f"{wl_name} (b {b}, h {h0}) sampled {n}")
+
+
+# ------------------------------------------------------- split of small grids
+
+def split_engaged(c):
+    """The sized workspace query reports room for partial gradients: the call will split."""
+    return (cpr.cp_ring_attn_bwd_workspace_size_ex(c.B, c.H, c.H_kv, c.D, c.lq, c.cp * c.lq) >
+            cpr.cp_ring_attn_bwd_workspace_size(c.B, c.H, c.lq))
+
+
+@pytest.mark.parametrize("case", ["example_4k", "gqa_docs_d128", "ragged_striped"])
+def test_bwd_split_small_grid(case):
+    """A bf16 backward on a grid too small for the GPU, given cp_ring_attn_bwd_workspace_size_ex bytes: the dQ
+    kernel splits over key slices and the dK/dV kernel over query slices, partials summed in slice order. It
+    must meet the oracle bar, agree with the unsplit call up to float32 summation order, and be deterministic."""
+    if case == "example_4k":     # the glossary page's 1 x 4 x 4096 x 64 example on two ranks
+        c = Case("bf16", 1, 4, 4, 64, 4096, 2, "zigzag", True, seed=320)
+    elif case == "gqa_docs_d128":
+        docs = [700, 3, 1200, 144, 1]
+        c = Case("bf16", 1, 4, 2, 128, sum(docs), 2, "zigzag", True, seed=321, docs=docs)
+    else:
+        c = Case("bf16", 2, 2, 2, 128, 1000, 4, "striped", True, seed=322)
+    assert split_engaged(c)
+    for r in range(c.cp) if c.cp <= 2 else (0, 3):
+        note(f"split {case} rank {r}")
+        ri, do_local, o_dev, lse_dev, kw, ref = c.rank(r)
+        got = c.run_gpu(r, ri, do_local, o_dev, lse_dev, kw, split=True)
+        again = c.run_gpu(r, ri, do_local, o_dev, lse_dev, kw, split=True)
+        plain = c.run_gpu(r, ri, do_local, o_dev, lse_dev, kw)
+        for g, g2, p, rf, z, n in zip(got, again, plain, ref, c.zero_rows, ("dQ", "dK", "dV")):
+            check(g, rf, "bf16", f"split {case} r{r} {n}", z)
+            assert np.array_equal(g, g2), f"{n}: split call not deterministic"
+            # only the float32 summation order of the slices differs from the unsplit call
+            assert np.abs(g - p).max() <= 1e-5 * np.abs(rf).max(), n
+
+
+def test_bwd_split_needs_the_whole_workspace():
+    """One byte short of cp_ring_attn_bwd_workspace_size_ex: the call runs unsplit (bit-identical to the base
+    workspace's result)."""
+    c = Case("bf16", 1, 4, 4, 64, 2048, 2, "zigzag", True, seed=323)
+    assert split_engaged(c)
+    ri, do_local, o_dev, lse_dev, kw, ref = c.rank(1)
+    full = cpr.cp_ring_attn_bwd_workspace_size_ex(c.B, c.H, c.H_kv, c.D, c.lq, c.cp * c.lq)
+    short = c.run_gpu(1, ri, do_local, o_dev, lse_dev, kw, ws_bytes=full - 1)
+    plain = c.run_gpu(1, ri, do_local, o_dev, lse_dev, kw)
+    for a, b in zip(short, plain):
+        assert np.array_equal(a, b)
+
+
+def test_bwd_step_split_accumulates():
+    """Per-block steps with the split workspace add their partial sums into the caller's accumulators, as the
+    unsplit steps do."""
+    c = Case("bf16", 1, 4, 2, 128, 1536, 3, "zigzag", True, seed=324)
+    r = 2
+    ri, do_local, o_dev, lse_dev, kw, ref = c.rank(r)
+    ws_bytes = cpr.cp_ring_attn_bwd_workspace_size_ex(c.B, c.H, c.H_kv, c.D, c.lq, c.lq)
+    assert ws_bytes > cpr.cp_ring_attn_bwd_workspace_size(c.B, c.H, c.lq)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    cpr.cp_ring_attn_bwd_prep(o_dev, do_local, lse_dev, ri.q_pos, True, ws)
+    dq = torch.zeros(ri.q_local.shape, dtype=torch.float32, device="cuda")
+    dk = torch.zeros(ri.k_ring.shape, dtype=torch.float32, device="cuda")
+    dv = torch.zeros(ri.v_ring.shape, dtype=torch.float32, device="cuda")
+    for t in range(c.cp):
+        src = (r - t) % c.cp
+        sl = slice(src * c.lq, (src + 1) * c.lq)
+        dk_blk = dk[:, :, sl].contiguous()
+        dv_blk = dv[:, :, sl].contiguous()
+        cpr.cp_ring_attn_bwd_step(ri.q_local, do_local, ri.k_ring[:, :, sl], ri.v_ring[:, :, sl], ri.ring_pos[sl],
+                                  0.0, ws, dq, dk_blk, dv_blk)
+        dk[:, :, sl] = dk_blk
+        dv[:, :, sl] = dv_blk
+    torch.cuda.synchronize()
+    for g, rf, z, n in zip((dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()), ref, c.zero_rows,
+                           ("dQ", "dK", "dV")):
+        check(g, rf, "bf16", f"split step {n}", z)
 
 
 def test_bwd_is_deterministic():
