@@ -7,6 +7,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <mutex>
 #include <string>
@@ -37,6 +38,24 @@ cpr_status ok() {
 cpr_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(CPR_EHIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+// With CPRING_SYNC_CHECK=1 in the environment, every call that launches work
+// waits for its stream before returning, so that a kernel failure (an illegal
+// address, say) is reported as CPR_EHIP by the call that launched it instead
+// of by a later call. A debugging aid: it makes every call synchronous.
+bool sync_check() {
+  const char* e = getenv("CPRING_SYNC_CHECK");
+  return e && e[0] == '1' && e[1] == 0;
+}
+
+// Status of a call whose last launch returned `e` on stream `st`.
+cpr_status launched(hipError_t e, hipStream_t st, const char* what) {
+  if (e == hipSuccess && sync_check()) {
+    e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  return hip_status(e, what);
 }
 
 bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
@@ -124,9 +143,9 @@ cpr_status cp_zigzag_partition(int64_t seq_len, int32_t cp_size, int32_t layout,
   if (!token_idx && !pos_ids) return fail(CPR_EINVAL, "token_idx and pos_ids are both NULL");
   if ((token_idx && !aligned(token_idx, 4)) || (pos_ids && !aligned(pos_ids, 4)))
     return fail(CPR_EINVAL, "output arrays must be 4-byte aligned");
-  return hip_status(launch_partition(seq_len, s_pad, cp_size, layout, token_idx, pos_ids,
+  return launched(launch_partition(seq_len, s_pad, cp_size, layout, token_idx, pos_ids,
                                      static_cast<hipStream_t>(stream)),
-                    "cp_zigzag_partition");
+                  static_cast<hipStream_t>(stream), "cp_zigzag_partition");
 }
 
 cpr_status cp_shard_gather(int32_t dtype, int32_t B, int32_t H, int64_t seq_len, int32_t D, const cpr_view* src,
@@ -142,9 +161,9 @@ cpr_status cp_shard_gather(int32_t dtype, int32_t B, int32_t H, int64_t seq_len,
   if (!token_idx) return fail(CPR_EINVAL, "token_idx is NULL");
   if (!dst) return fail(CPR_EINVAL, "dst is NULL");
   if (!aligned(dst, 16)) return fail(CPR_EINVAL, "dst must be 16-byte aligned");
-  return hip_status(launch_gather(esize_of(dtype), B, H, seq_len, D, *src, token_idx, n_out, dst,
+  return launched(launch_gather(esize_of(dtype), B, H, seq_len, D, *src, token_idx, n_out, dst,
                                   static_cast<hipStream_t>(stream)),
-                    "cp_shard_gather");
+                  static_cast<hipStream_t>(stream), "cp_shard_gather");
 }
 
 cpr_status cp_ring_attn_init(int32_t B, int32_t H, int32_t Lq, int32_t D, float* o_acc, float* m, float* l,
@@ -153,8 +172,8 @@ cpr_status cp_ring_attn_init(int32_t B, int32_t H, int32_t Lq, int32_t D, float*
   TRY(check_len("Lq", Lq));
   TRY(check_state(0, o_acc, m, l));
   const int64_t rows = (int64_t)B * H * Lq;
-  return hip_status(launch_state_init(rows, D, o_acc, m, l, static_cast<hipStream_t>(stream)),
-                    "cp_ring_attn_init");
+  return launched(launch_state_init(rows, D, o_acc, m, l, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream), "cp_ring_attn_init");
 }
 
 // need_q_pos = 0 for calls that take no query positions (the backward step,
@@ -223,7 +242,8 @@ cpr_status cp_ring_attn_step_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, 
   a.nblocks = 1; a.rank = 0; a.cp = 1;
   a.o_acc = o_acc; a.m = m; a.l = l;
   a.load_state = 1; a.finalize = 0;
-  return hip_status(launch_attn(dtype, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_step");
+  return launched(launch_attn(dtype, a, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream), "cp_ring_attn_step");
 }
 
 cpr_status cp_ring_attn_merge(int32_t B, int32_t H, int32_t Lq, int32_t D, float* o_acc, float* m, float* l,
@@ -234,8 +254,8 @@ cpr_status cp_ring_attn_merge(int32_t B, int32_t H, int32_t Lq, int32_t D, float
   if (!o2 || !m2 || !l2) return fail(CPR_EINVAL, "partial-state pointers must be non-NULL");
   if (!aligned(o2, 16) || !aligned(m2, 4) || !aligned(l2, 4)) return fail(CPR_EINVAL, "o2 must be 16-byte aligned");
   const int64_t rows = (int64_t)B * H * Lq;
-  return hip_status(launch_merge(rows, D, o_acc, m, l, o2, m2, l2, static_cast<hipStream_t>(stream)),
-                    "cp_ring_attn_merge");
+  return launched(launch_merge(rows, D, o_acc, m, l, o2, m2, l2, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream), "cp_ring_attn_merge");
 }
 
 cpr_status cp_ring_attn_finalize(int32_t out_dtype, int32_t B, int32_t H, int32_t Lq, int32_t D,
@@ -248,9 +268,9 @@ cpr_status cp_ring_attn_finalize(int32_t out_dtype, int32_t B, int32_t H, int32_
   if (!aligned(o_out, 16)) return fail(CPR_EINVAL, "o_out must be 16-byte aligned");
   if (lse_out && !aligned(lse_out, 4)) return fail(CPR_EINVAL, "lse_out must be 4-byte aligned");
   const int64_t rows = (int64_t)B * H * Lq;
-  return hip_status(launch_finalize(out_dtype == CPR_BF16, rows, D, o_acc, m, l, o_out, lse_out,
+  return launched(launch_finalize(out_dtype == CPR_BF16, rows, D, o_acc, m, l, o_out, lse_out,
                                     static_cast<hipStream_t>(stream)),
-                    "cp_ring_attn_finalize");
+                  static_cast<hipStream_t>(stream), "cp_ring_attn_finalize");
 }
 
 static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -310,12 +330,12 @@ static cpr_status run_fused(int32_t dtype, AttnArgs a, int32_t cp_size, int32_t 
     a.load_state = 0; a.finalize = 0;
     const hipError_t e = launch_attn(dtype, a, st);
     if (e != hipSuccess) return hip_status(e, "cp_ring_attn_run");
-    return hip_status(launch_merge_finalize(1, ns, (int64_t)rows, a.D, a.o_acc, a.m, a.l, o_out, lse_out, st),
-                      "cp_ring_attn_run(merge)");
+    return launched(launch_merge_finalize(1, ns, (int64_t)rows, a.D, a.o_acc, a.m, a.l, o_out, lse_out, st),
+                    st, "cp_ring_attn_run(merge)");
   }
   a.o_out = o_out; a.lse = lse_out;
   a.load_state = 0; a.finalize = 1;
-  return hip_status(launch_attn(dtype, a, st), "cp_ring_attn_run");
+  return launched(launch_attn(dtype, a, st), st, "cp_ring_attn_run");
 }
 
 cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, int32_t cp_size, int32_t rank,
@@ -348,8 +368,8 @@ cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, i
     e = launch_attn(dtype, a, st);
     if (e != hipSuccess) return hip_status(e, "cp_ring_attn_run(step)");
   }
-  return hip_status(launch_finalize(dtype == CPR_BF16, (int64_t)rows, D, o_acc, m, l, o_out, lse_out, st),
-                    "cp_ring_attn_run(finalize)");
+  return launched(launch_finalize(dtype == CPR_BF16, (int64_t)rows, D, o_acc, m, l, o_out, lse_out, st),
+                  st, "cp_ring_attn_run(finalize)");
 }
 
 }  // extern "C"
@@ -527,7 +547,8 @@ cpr_status cp_ring_attn_bwd_prep(int32_t dtype, int32_t B, int32_t H, int32_t D,
   a.causal = causal ? 1 : 0;
   a.B = B; a.H = H; a.D = D; a.Lq = Lq;
   bwd_workspace(workspace, B, H, Lq, &a.lse2, &a.dvec, &a.qwin);
-  return hip_status(launch_bwd_prep(dtype == CPR_BF16, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_bwd_prep");
+  return launched(launch_bwd_prep(dtype == CPR_BF16, a, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream), "cp_ring_attn_bwd_prep");
 }
 
 static BwdArgs make_bwd_args(int32_t B, int32_t H, int32_t D, int32_t H_kv, const cpr_view* q,
@@ -574,7 +595,8 @@ cpr_status cp_ring_attn_bwd_step(int32_t dtype, int32_t B, int32_t H, int32_t D,
   a.dq = dq_acc; a.dk = dk_acc; a.dv = dv_acc;
   a.accumulate = 1;
   bwd_plan_split(dtype, a, Lk, const_cast<void*>(workspace), workspace_bytes);
-  return hip_status(launch_bwd(dtype, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_bwd_step");
+  return launched(launch_bwd(dtype, a, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream), "cp_ring_attn_bwd_step");
 }
 
 cpr_status cp_ring_attn_bwd_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
@@ -604,7 +626,8 @@ cpr_status cp_ring_attn_bwd_run(int32_t dtype, int32_t B, int32_t H, int32_t D,
   a.dq = dq_local; a.dk = dk_ring; a.dv = dv_ring;
   a.accumulate = 0;
   bwd_plan_split(dtype, a, (int64_t)Lq * cp_size, workspace, workspace_bytes);
-  return hip_status(launch_bwd(dtype, a, static_cast<hipStream_t>(stream)), "cp_ring_attn_bwd_run");
+  return launched(launch_bwd(dtype, a, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream), "cp_ring_attn_bwd_run");
 }
 
 cpr_status cp_rope_apply(int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t D, const cpr_view* x,
@@ -625,7 +648,8 @@ cpr_status cp_rope_apply(int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t
   a.base = base;
   a.style = style;
   a.out = out;
-  return hip_status(launch_rope(dtype == CPR_BF16, a, static_cast<hipStream_t>(stream)), "cp_rope_apply");
+  return launched(launch_rope(dtype == CPR_BF16, a, static_cast<hipStream_t>(stream)),
+                  static_cast<hipStream_t>(stream), "cp_rope_apply");
 }
 
 const char* cp_status_string(int32_t status) {

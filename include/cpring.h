@@ -32,7 +32,10 @@
  *    scratch array of cp_ring_attn_run_noalloc (loaded with the library).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream) and does not synchronise. Results are valid once the stream has
- *    reached the call.
+ *    reached the call. Debugging aid: with CPRING_SYNC_CHECK=1 in the
+ *    environment, every call that launches work waits for its stream before
+ *    it returns, so that a failure of its kernels is reported as CPR_EHIP by
+ *    that call rather than by a later one.
  *  - Arguments are validated before anything is launched. On failure the call
  *    returns a non-zero cpr_status, launches nothing, and cp_last_error()
  *    describes the problem. A launch failure returns CPR_EHIP. No C++

@@ -21,10 +21,13 @@ HEADER = os.path.join(ROOT, "include", "cpring.h")
 
 @pytest.fixture(scope="module")
 def lib():
-    if not os.path.exists(cpr.LIB_PATH):
+    # CPRING_TEST_LIB: run these checks against another build of the library
+    # (the host-AddressSanitizer build of tests/test_host_asan.py)
+    path = os.environ.get("CPRING_TEST_LIB", cpr.LIB_PATH)
+    if path == cpr.LIB_PATH and not os.path.exists(path):
         from context_ring_attention_zigzag_amd import build
         build.build()
-    return cpr.load()
+    return cpr.load(path)
 
 
 def header_functions():
@@ -38,7 +41,8 @@ def test_header_and_binding_agree():
 
 
 def test_library_exports_every_declared_symbol(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", cpr.LIB_PATH], capture_output=True, text=True, check=True)
+    path = os.environ.get("CPRING_TEST_LIB", cpr.LIB_PATH)
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True)
     exported = {line.split()[-1] for line in out.stdout.splitlines() if line.strip()}
     for name in header_functions():
         assert name in exported, name

@@ -571,3 +571,32 @@ def test_fused_and_stepwise_agree():
     a, la, _ = run_rank(w, dev, 3, cpr.RUN_FUSED)
     b, lb, _ = run_rank(w, dev, 3, cpr.RUN_STEPWISE)
     assert np.abs(a - b).max() <= 1e-2 and np.abs(la - lb).max() <= 1e-4
+
+
+def test_sync_check_mode_same_results(monkeypatch):
+    """CPRING_SYNC_CHECK=1: every launching call waits for its stream before it returns (so a kernel failure is
+    reported by the call that launched it). The results are the same bits; the forward, the split fused run
+    and the backward all pass through it."""
+    w = small_workload("sync_check", "bf16", 1, 4, 128, 3000, 2, "zigzag", True, seed=61)
+    dev, _ = natural_inputs(w)
+
+    def both():
+        o, lse, ri = run_rank(w, dev, 1, SPLIT)
+        o2, lse2, _ = run_rank(w, dev, 1, cpr.RUN_STEPWISE)
+        lq = ri.lq
+        ws = torch.empty(cpr.cp_ring_attn_bwd_workspace_size_ex(w.B, w.H, w.H, w.D, lq, w.cp * lq),
+                         dtype=torch.uint8, device="cuda")
+        o_t = torch.from_numpy(o).to(torch.bfloat16).cuda()
+        g = [torch.empty(ri.q_local.shape, device="cuda"), torch.empty(ri.k_ring.shape, device="cuda"),
+             torch.empty(ri.v_ring.shape, device="cuda")]
+        cpr.cp_ring_attn_bwd_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, 1, o_t, o_t,
+                                 torch.from_numpy(lse).cuda(), True, 0.0, *g, ws)
+        torch.cuda.synchronize()
+        return [o, lse, o2, lse2] + [x.cpu().numpy() for x in g]
+
+    monkeypatch.delenv("CPRING_SYNC_CHECK", raising=False)
+    plain = both()
+    monkeypatch.setenv("CPRING_SYNC_CHECK", "1")
+    checked = both()
+    for a, b in zip(plain, checked):
+        assert np.array_equal(a, b)
