@@ -33,7 +33,7 @@ EXPORTS = (
     "cp_ring_attn_merge", "cp_ring_attn_finalize", "cp_ring_attn_workspace_size", "cp_ring_attn_run",
     "cp_ring_attn_step_ex", "cp_ring_attn_run_ex", "cp_ring_attn_run_noalloc", "cp_ring_attn_bwd_workspace_size",
     "cp_ring_attn_bwd_workspace_size_ex", "cp_ring_attn_bwd_prep",
-    "cp_ring_attn_bwd_step", "cp_ring_attn_bwd_run", "cp_rope_apply", "cp_status_string", "cp_last_error",
+    "cp_ring_attn_bwd_step", "cp_ring_attn_bwd_run", "cp_rope_apply", "cp_ring_attn_tile_census", "cp_status_string", "cp_last_error",
 )
 
 
@@ -92,6 +92,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "cp_ring_attn_bwd_run": (i32, [i32, i32, i32, i32, i32, i32, pv, i32, vp, pv, pv, vp, pv, pv, vp, i32, f32,
                                        pe, vp, vp, vp, vp, ctypes.c_size_t, vp]),
         "cp_rope_apply": (i32, [i32, i32, i32, i32, i32, pv, vp, f32, i32, vp, vp]),
+        "cp_ring_attn_tile_census": (i32, [i32, i32, vp, vp, i32, pe, vp, vp, vp]),
         "cp_status_string": (ctypes.c_char_p, [i32]),
         "cp_last_error": (ctypes.c_char_p, []),
     }
@@ -308,3 +309,19 @@ def cp_rope_apply(x, pos, out=None, base: float = 10000.0, style: int = ROPE_INT
     _check(load().cp_rope_apply(dtype_code(x), B, H, L, D, ctypes.byref(xv), _ptr(pos), float(base), int(style),
                                 _ptr(out), _stream(stream)), "cp_rope_apply")
     return out
+
+
+# ------------------------------------------------------------- tile census
+
+def cp_ring_attn_tile_census(q_pos, ring_pos, cp_size: int, causal: bool, kw_lo=None, kw_hi=None, stream=None):
+    """(kept, masked): int32 device tensors with, per 256-query tile, the 64-key tiles the bf16 forward pass
+    computes over all blocks and how many of those need the element mask."""
+    lq = q_pos.numel()
+    nqt = (lq + 255) // 256
+    kept = torch.empty(nqt, dtype=torch.int32, device=q_pos.device)
+    masked = torch.empty(nqt, dtype=torch.int32, device=q_pos.device)
+    ext = None if kw_lo is None and kw_hi is None else _win_ext(0, kw_lo, kw_hi)
+    _check(load().cp_ring_attn_tile_census(cp_size, lq, _ptr(q_pos), _ptr(ring_pos), int(bool(causal)),
+                                           None if ext is None else ctypes.byref(ext), _ptr(kept), _ptr(masked),
+                                           _stream(stream)), "cp_ring_attn_tile_census")
+    return kept, masked

@@ -652,6 +652,29 @@ cpr_status cp_rope_apply(int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t
                   static_cast<hipStream_t>(stream), "cp_rope_apply");
 }
 
+cpr_status cp_ring_attn_tile_census(int32_t cp_size, int32_t Lq, const int32_t* q_pos, const int32_t* ring_pos,
+                                    int32_t causal, const cpr_attn_ext* ext, int32_t* kept, int32_t* masked,
+                                    void* stream) {
+  if (cp_size < 1) return fail(CPR_EINVAL, "cp_size must be >= 1 (got %d)", cp_size);
+  TRY(check_len("Lq", Lq));
+  if ((int64_t)Lq * cp_size > CPR_MAX_SEQ) return fail(CPR_EUNSUPPORTED, "cp_size * Lq must be <= 2^30");
+  if (!q_pos || !ring_pos) return fail(CPR_EINVAL, "position arrays must be non-NULL");
+  if (!kept || !masked) return fail(CPR_EINVAL, "kept and masked must be non-NULL");
+  if (!aligned(kept, 4) || !aligned(masked, 4)) return fail(CPR_EINVAL, "kept and masked must be 4-byte aligned");
+  if (ext && ((ext->kw_lo && !aligned(ext->kw_lo, 4)) || (ext->kw_hi && !aligned(ext->kw_hi, 4))))
+    return fail(CPR_EINVAL, "key-window arrays must be 4-byte aligned");
+  CensusArgs a{};
+  a.q_pos = q_pos;
+  a.kv_pos = ring_pos;
+  a.kw_lo = ext ? ext->kw_lo : nullptr;
+  a.kw_hi = ext ? ext->kw_hi : nullptr;
+  a.Lq = Lq; a.Lk = Lq; a.nblocks = cp_size;
+  a.causal = causal ? 1 : 0;
+  a.kept = kept; a.masked = masked;
+  return launched(launch_tile_census(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream),
+                  "cp_ring_attn_tile_census");
+}
+
 const char* cp_status_string(int32_t status) {
   switch (status) {
     case CPR_OK: return "ok";

@@ -58,6 +58,7 @@
 
 #include "common.h"
 #include "mfma_util.h"
+#include "tile_class.h"
 
 namespace cpring {
 namespace {
@@ -65,8 +66,8 @@ namespace {
 using namespace mfma;
 
 constexpr float kTau = 8.0f;    // lazy-rescale threshold: probabilities stay below 2^kTau
-constexpr int kBN = 64;         // keys per tile
-constexpr int kMaxTiles = 4096; // key tiles classified per segment of a KV block
+constexpr int kBN = tiles::kKeyTile;          // keys per tile (64)
+constexpr int kMaxTiles = tiles::kSegTiles;   // key tiles classified per segment of a KV block (4096)
 constexpr int kListPad = 8;     // end markers after the last kept tile (look-ahead reads)
 #ifndef CPR_M_PREFETCH
 #define CPR_M_PREFETCH 5
@@ -140,44 +141,14 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   const int q_base = qt * C::kBM;
   const int q_idx = q_base + wave * 32 + ql;
   const bool q_in = q_idx < a.Lq;
-  const int32_t qp = q_in ? a.q_pos[q_idx] : -1;
   // key positions this query may attend, [qlow, qlim]: the causal bound and the
-  // optional per-query window; empty (qlim = -1) for a pad query. qlow >= 0,
-  // so pad keys (position -1) always fall outside.
-  int32_t qlow = 0, qlim = -1;
-  if (qp >= 0) {
-    qlow = a.kw_lo ? max(a.kw_lo[q_idx], 0) : 0;
-    qlim = a.causal ? qp : INT_MAX;
-    if (a.kw_hi) qlim = min(qlim, a.kw_hi[q_idx]);
-  }
+  // optional per-query window; empty for a pad query
+  int32_t qlow, qlim;
+  tiles::query_window(a.q_pos, a.kw_lo, a.kw_hi, a.causal, q_idx, q_in, qlow, qlim);
   const bool q_live = qlow <= qlim;   // attends some key position
 
-  // ---- bounds over the workgroup's live queries: the lowest and highest
-  // allowed key position any query may attend (lb_min, ub_max) and every query
-  // may attend (lb_max, ub_min)
-  int lb_min, lb_max, ub_min, ub_max;
-  {
-    const int w0 = wave_min(q_live ? qlow : INT_MAX), w1 = wave_max(q_live ? qlow : -1);
-    const int w2 = wave_min(q_live ? qlim : INT_MAX), w3 = wave_max(q_live ? qlim : -1);
-    if (lane == 0) {
-      qrange[0][wave] = w0;
-      qrange[1][wave] = w1;
-      qrange[2][wave] = w2;
-      qrange[3][wave] = w3;
-    }
-    __syncthreads();
-    lb_min = INT_MAX;
-    lb_max = -1;
-    ub_min = INT_MAX;
-    ub_max = -1;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      lb_min = min(lb_min, qrange[0][w]);
-      lb_max = max(lb_max, qrange[1][w]);
-      ub_min = min(ub_min, qrange[2][w]);
-      ub_max = max(ub_max, qrange[3][w]);
-    }
-  }
+  // ---- bounds over the workgroup's live queries (tile classification)
+  const tiles::QBounds qb = tiles::workgroup_bounds<NW>(q_live, qlow, qlim, qrange);
 
   // ---- resident Q fragments (B operand of S^T = K Q^T): d = 16*kk + 8*hh + e
   bf16x8 qf[C::kKSteps];
@@ -224,7 +195,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;   // finite stand-in while nothing is allowed yet
 
   const float c2 = a.scale * kLog2e;   // score -> log2 units
-  const bool wg_has_queries = ub_max >= 0;
+  const bool wg_has_queries = qb.ub_max >= 0;
 
   const int hk = h / (a.H / a.H_kv);   // grouped-query attention: the K/V head of query head h
   const __bf16* kbh = static_cast<const __bf16*>(a.k) + b * a.k_sb + hk * a.k_sh;
@@ -274,41 +245,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
     for (int seg0 = kt_lo; seg0 < kt_hi; seg0 += kMaxTiles) {
       const int nseg = min(kMaxTiles, kt_hi - seg0);
 
-      // ---- classify the segment's key tiles: 16 lanes per tile, 4 positions each
+      // ---- classify the segment's key tiles
       bar();   // the previous segment is done with flags8 / klist / the buffers
-      for (int base = 0; base < nseg; base += kThreads / 16) {
-        const int tt = base + (tid >> 4);
-        const int g16 = tid & 15;
-        int kmin = INT_MAX, kmax = -1, pad = 0;
-        if (tt < nseg) {
-          const int k0 = (seg0 + tt) * kBN + 4 * g16;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int j = k0 + e;
-            if (j < a.Lk) {
-              const int p = posb[j];
-              pad |= p < 0;
-              kmin = (p >= 0 && p < kmin) ? p : kmin;
-              kmax = p > kmax ? p : kmax;
-            } else {
-              pad = 1;
-            }
-          }
-        }
-#pragma unroll
-        for (int o = 8; o >= 1; o >>= 1) {
-          kmin = min(kmin, __shfl_xor(kmin, o));
-          kmax = max(kmax, __shfl_xor(kmax, o));
-          pad |= __shfl_xor(pad, o);
-        }
-        if (g16 == 0 && tt < nseg) {
-          // kept when the tile's positions meet some query's allowed range; full
-          // when every live query may attend every key of the tile
-          const bool keep = kmax >= 0 && kmax >= lb_min && kmin <= ub_max;
-          const bool full = !pad && kmin >= lb_max && kmax <= ub_min;
-          flags8[tt] = (uint8_t)((keep ? 1 : 0) | ((keep && !full) ? 2 : 0));
-        }
-      }
+      tiles::classify_key_tiles<kThreads, kBN>(posb, seg0, nseg, a.Lk, qb, flags8);
       bar();
 
       // ---- ordered list of the kept tiles (entry = tile index, | 0x8000 when the
@@ -684,9 +623,12 @@ int32_t attn_bf16_kv_split(int32_t B, int32_t H, int32_t Lq, int32_t Lk) {
   return (int32_t)std::min(std::min(kCUs / grid, n_kt), kMaxSplit);
 }
 
+static_assert(Cfg<128, tiles::kWaves>::kBM == tiles::kQueryTile && Cfg<64, tiles::kWaves>::kBM == tiles::kQueryTile,
+              "the tile census describes this kernel's query tiles");
+
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st) {
-  if (a.D == 64) return launch<64, 8>(a, st);
-  return launch<128, 8>(a, st);
+  if (a.D == 64) return launch<64, tiles::kWaves>(a, st);
+  return launch<128, tiles::kWaves>(a, st);
 }
 
 }  // namespace cpring

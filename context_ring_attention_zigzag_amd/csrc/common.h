@@ -121,6 +121,17 @@ struct RopeArgs {
 };
 hipError_t launch_rope(int32_t dtype_bf16, const RopeArgs& a, hipStream_t st);
 
+// Tile census of the bf16 forward pass over nblocks blocks of Lk keys
+// (kv_pos holds nblocks * Lk positions): kept[qt] and masked[qt] for every
+// 256-query tile qt.
+struct CensusArgs {
+  const int32_t* q_pos; const int32_t* kv_pos;
+  const int32_t* kw_lo; const int32_t* kw_hi;
+  int32_t Lq, Lk, nblocks, causal;
+  int32_t* kept; int32_t* masked;
+};
+hipError_t launch_tile_census(const CensusArgs& a, hipStream_t st);
+
 hipError_t launch_attn_bf16(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_f32(const AttnArgs& a, hipStream_t st);
 

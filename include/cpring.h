@@ -421,6 +421,26 @@ typedef enum {
 cpr_status cp_rope_apply(int32_t dtype, int32_t B, int32_t H, int32_t L, int32_t D, const cpr_view* x,
                          const int32_t* pos, float base, int32_t style, void* out, void* stream);
 
+/*
+ * Tile census of the bf16 forward pass of cp_ring_attn_run_ex over the same
+ * positions (q_pos [Lq], ring_pos [cp_size * Lq], causal, and the windows of
+ * ext; H_kv is ignored): the pass takes its queries in tiles of 256 and the
+ * keys of every block in tiles of 64, and classifies every (query tile, key
+ * tile) pair from position ranges as skipped (no query of the tile may attend
+ * any of its keys: neither loaded nor computed), full (computed without the
+ * element mask) or masked (computed with the element mask). For every query
+ * tile qt (ceil(Lq / 256) of them) this writes to the int32 device arrays
+ *   kept[qt]    the key tiles computed, over all cp_size blocks,
+ *   masked[qt]  those of them that need the element mask,
+ * with the forward kernel's own classification code. The Megatron page
+ * ("Implementation quirk: symmetric chunk assignment") pairs chunks r and
+ * 2cp-1-r so that every rank does the same causal work; the census shows it
+ * at tile granularity (the same sum on every rank). B, H and D do not enter.
+ */
+cpr_status cp_ring_attn_tile_census(int32_t cp_size, int32_t Lq, const int32_t* q_pos, const int32_t* ring_pos,
+                                    int32_t causal, const cpr_attn_ext* ext, int32_t* kept, int32_t* masked,
+                                    void* stream);
+
 /* Static description of a status code. */
 const char* cp_status_string(int32_t status);
 
