@@ -66,6 +66,7 @@ namespace {
 using namespace mfma;
 
 constexpr float kTau = 8.0f;    // lazy-rescale threshold: probabilities stay below 2^kTau
+constexpr float kGuard = 256.0f;   // 2^kTau: a lane's probability sum under it bounds each probability
 constexpr int kBN = tiles::kKeyTile;          // keys per tile (64)
 constexpr int kMaxTiles = tiles::kSegTiles;   // key tiles classified per segment of a KV block (4096)
 constexpr int kListPad = 8;     // end markers after the last kept tile (look-ahead reads)
@@ -91,7 +92,12 @@ struct Cfg {
 };
 
 
-template <int D, int NW, bool SPLIT>
+// EXACT: every tile's row max is taken (needed when the launch hands back the
+// state (O, m, l) with m the true running max: a ring step). Otherwise (a
+// fused run, which finalises, or a split launch, whose partial states the
+// merge rescales from any reference) the row max is taken only when a tile's
+// probability sum says the reference may be too low, see softmax_guarded.
+template <int D, int NW, bool SPLIT, bool EXACT>
 __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
   using C = Cfg<D, NW>;
   constexpr int kThreads = C::kThreads;
@@ -376,10 +382,9 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         return fmaxf(m0, m1);
       };
       // mxh: row max of the unmasked scores, taken in the MFMA phase
-      auto softmax_max = [&](f32x16 (&s)[2], int e, int pslot, float mxh) __attribute__((always_inline)) {
-        if (e & 0x8000) {
-          // element mask of a tile straddling the causal boundary or holding
-          // pads / rows past Lk; the row max is taken again over what is left
+      // element mask of a tile straddling the causal boundary or holding pads /
+      // rows past Lk: scores of keys the query may not attend become -inf
+      auto apply_mask = [&](f32x16 (&s)[2], int e, int pslot) __attribute__((always_inline)) {
           const int32_t* pl = &pos_lds[pslot][4 * hh];
           // keys of this tile that exist, less this half-wave's key offset: key
           // kt*32 + 8*i + 4*hh + jj exists when kt*32 + 8*i + jj < remh
@@ -396,6 +401,25 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
                 s[kt][4 * i + jj] = ok ? s[kt][4 * i + jj] : -INFINITY;
               }
             }
+      };
+      // raise the reference max of the rows whose max mt (log2 units) outgrew it
+      // by more than kTau: O and l are rescaled by 2^(m_ref - m_new)
+      auto raise_ref = [&](bool up, float mt) __attribute__((always_inline)) {
+        const float m_new = up ? mt : m_ref;
+        const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+        for (int dt = 0; dt < C::kDTiles; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) ot[dt][i] *= alpha;
+        lsum0 *= alpha;
+        lsum1 *= alpha;
+        m_ref = m_new;
+        m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
+      };
+      auto softmax_max = [&](f32x16 (&s)[2], int e, int pslot, float mxh) __attribute__((always_inline)) {
+        if (e & 0x8000) {
+          // the row max is taken again over what the mask leaves
+          apply_mask(s, e, pslot);
           mxh = row_max(s);
         }
         const float mx = other_half_max(mxh);
@@ -403,23 +427,13 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         const float mt = mx * c2;
         m_true = fmaxf(m_true, mt);
         const bool need = mt > m_ref + kTau;
-        if (__any(need)) {
-          const float m_new = need ? mt : m_ref;
-          const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-#pragma unroll
-          for (int dt = 0; dt < C::kDTiles; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) ot[dt][i] *= alpha;
-          lsum0 *= alpha;
-          lsum1 *= alpha;
-          m_ref = m_new;
-          m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-        }
+        if (__any(need)) raise_ref(need, mt);
       };
       // ---- VALU phase, second part, 16 keys at a time: P = 2^(s*c2 - m_ref)
       // rounded to bf16, in the B-operand layout of O^T += V^T P^T; l accumulates
       // the same values before rounding
-      auto softmax_exp = [&](const f32x16 (&s)[2], bf16x8 (&pb)[4], auto chunk, float mu) __attribute__((always_inline)) {
+      auto softmax_exp = [&](const f32x16 (&s)[2], bf16x8 (&pb)[4], auto chunk, float mu, float& acc0, float& acc1)
+          __attribute__((always_inline)) {
         constexpr int c = decltype(chunk)::value;
         uint32_t w4[4];
 #pragma unroll
@@ -427,11 +441,47 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
           const float e0 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + 2 * x], c2, -mu));
           const float e1 = __builtin_amdgcn_exp2f(fmaf(s[c >> 1][8 * (c & 1) + 2 * x + 1], c2, -mu));
           const bf16x2 pr = {(__bf16)e0, (__bf16)e1};
-          lsum0 += e0;
-          lsum1 += e1;
+          acc0 += e0;
+          acc1 += e1;
           w4[x] = __builtin_bit_cast(uint32_t, pr);
         }
         pb[c] = __builtin_bit_cast(bf16x8, w4);
+      };
+      auto softmax_exp4 = [&](const f32x16 (&s)[2], bf16x8 (&pb)[4], float mu, float& acc0, float& acc1)
+          __attribute__((always_inline)) {
+        softmax_exp(s, pb, ic<0>{}, mu, acc0, acc1);
+        softmax_exp(s, pb, ic<1>{}, mu, acc0, acc1);
+        softmax_exp(s, pb, ic<2>{}, mu, acc0, acc1);
+        softmax_exp(s, pb, ic<3>{}, mu, acc0, acc1);
+      };
+      // Exponentials against the current reference, with no row max: the tile's
+      // probabilities are summed per lane first. A lane's 32 probabilities all
+      // stay below 2^kTau when their sum does, which is the bound the exact rule
+      // (raise the reference when the row max outgrows it by kTau) keeps; only
+      // when some lane's sum exceeds it, or a row has no reference yet, is the
+      // exact rule applied, and the exponentials redone if it raised a reference.
+      auto softmax_guarded = [&](f32x16 (&s)[2], bf16x8 (&pb)[4], int e, int pslot) __attribute__((always_inline)) {
+        if (e & 0x8000) apply_mask(s, e, pslot);
+        float t0 = 0.f, t1 = 0.f;
+        softmax_exp4(s, pb, m_use, t0, t1);
+        const bool check = m_ref == -INFINITY || !(t0 + t1 <= kGuard);
+        if (__any(check)) {
+          // the scores pass through an empty asm statement, so that the compiler
+          // cannot take the row max ahead of the branch, on the fast path
+          f32x16 sx[2] = {s[0], s[1]};
+#if defined(__HIP_DEVICE_COMPILE__)
+          asm volatile("" : "+v"(sx[0]), "+v"(sx[1]));
+#endif
+          const float mt = other_half_max(row_max(sx)) * c2;
+          const bool up = mt > m_ref + kTau;
+          if (__any(up)) {
+            raise_ref(up, mt);
+            t0 = t1 = 0.f;
+            softmax_exp4(sx, pb, m_use, t0, t1);
+          }
+        }
+        lsum0 += t0;
+        lsum1 += t1;
       };
 
       // Empty asm statements that read the given registers: the values must be
@@ -475,13 +525,12 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       auto vphase = [&](bool has, float mxh) __attribute__((always_inline)) {
         const int ahead = klist[u + 4];              // read now, used at the end
         if (has) {
-          float mu;
-          softmax_max(s, e0, u & 3, mxh);
-          mu = m_use;
-          softmax_exp(s, pb, ic<0>{}, mu);
-          softmax_exp(s, pb, ic<1>{}, mu);
-          softmax_exp(s, pb, ic<2>{}, mu);
-          softmax_exp(s, pb, ic<3>{}, mu);
+          if constexpr (EXACT) {
+            softmax_max(s, e0, u & 3, mxh);
+            softmax_exp4(s, pb, m_use, lsum0, lsum1);
+          } else {
+            softmax_guarded(s, pb, e0, u & 3);
+          }
         }
         // (lands by the end of this wave's next MFMA phase, with the tile loads)
         if (wave == NW - 1) load_pos(tix(e3), (u + 3) & 3);
@@ -519,7 +568,8 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
 
       // tile 0: no P*V yet
       mphase(ic<0>{}, ic<2>{}, ic<0>{}, s, pb, [&](int m) { mloads(ic<0>{}, m, 2 * C::kKSteps); });
-      float mxh = row_max(s);
+      float mxh = 0.f;
+      if constexpr (EXACT) mxh = row_max(s);
       pin_scores(s, mxh);
       vm_wait<2 * C::kLoadsPerWave>();
       bar();
@@ -536,7 +586,7 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         mphase(ic<KS>{}, ic<(KS + 2) % 3>{}, ic<1>{}, s, pb,
                [&](int m) { mloads(kslot, m, 2 * C::kKSteps + C::kNB); });
         // the row max of the new scores, beside the P*V MFMAs of this phase
-        mxh = row_max(s);
+        if constexpr (EXACT) mxh = row_max(s);
         pin_scores(s, mxh);
         // this wave's tile loads of the previous MFMA phase have landed
         vm_wait<2 * C::kLoadsPerWave>();
@@ -576,8 +626,11 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
       }
     if (a.lse && hh == 0) a.lse[srow] = has ? (m_ref + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   } else {
-    // hand back the state against the true running max: O and l scale by 2^(m_ref - m_true) <= 1
-    const float beta = has ? __builtin_amdgcn_exp2f(m_ref - m_true) : 0.f;
+    // hand back the state against the true running max (O and l scale by
+    // 2^(m_ref - m_true) <= 1); a split launch's partial states keep the
+    // reference, which the merge rescales like any other max
+    const float m_out = EXACT ? m_true : m_ref;
+    const float beta = has ? (EXACT ? __builtin_amdgcn_exp2f(m_ref - m_true) : 1.f) : 0.f;
     const int64_t prow = SPLIT ? srow + (int64_t)slice * a.state_rows : srow;   // this slice's partial state
 #pragma unroll
     for (int dt = 0; dt < C::kDTiles; ++dt)
@@ -588,21 +641,32 @@ __global__ void __launch_bounds__(NW * 64, 1) attn_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<float4*>(a.o_acc + prow * D + 32 * dt + 8 * i + 4 * hh) = x;
       }
     if (hh == 0) {
-      a.m[prow] = has ? m_true * kLn2 : -INFINITY;
+      a.m[prow] = has ? m_out * kLn2 : -INFINITY;
       a.l[prow] = has ? l_tot * beta : 0.f;
     }
   }
 }
+
+// The guarded softmax (no row max per tile) pays off where the vector phase
+// sets the pace, at D = 64: 2.4% faster on the non-causal 65,536-token shape.
+// At D = 128 the matrix phase is the longer one and the guard measured 0.5%
+// slower there and 2.2% slower on the million-token share, so D = 128 keeps
+// the row max.
+template <int D>
+constexpr bool kGuarded = D == 64;
 
 template <int D, int NW>
 hipError_t launch(const AttnArgs& a, hipStream_t st) {
   const int nqt = (a.Lq + Cfg<D, NW>::kBM - 1) / Cfg<D, NW>::kBM;
   if (a.kv_split > 1) {
     const dim3 grid((unsigned)(nqt * a.B * a.H * a.kv_split));
-    hipLaunchKernelGGL((attn_bf16_kernel<D, NW, true>), grid, dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NW, true, !kGuarded<D>>), grid, dim3(NW * 64), 0, st, a);
+  } else if (a.finalize) {
+    const dim3 grid((unsigned)(nqt * a.B * a.H));
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NW, false, !kGuarded<D>>), grid, dim3(NW * 64), 0, st, a);
   } else {
     const dim3 grid((unsigned)(nqt * a.B * a.H));
-    hipLaunchKernelGGL((attn_bf16_kernel<D, NW, false>), grid, dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_bf16_kernel<D, NW, false, true>), grid, dim3(NW * 64), 0, st, a);
   }
   return hipGetLastError();
 }

@@ -600,3 +600,37 @@ def test_sync_check_mode_same_results(monkeypatch):
     checked = both()
     for a, b in zip(plain, checked):
         assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_rescale_paths_with_structured_scores(d):
+    """Scores built to drive every branch of the lazy rescale: every query is the same vector u and key j is
+    t_j u / (c |u|^2) with c = log2(e)/sqrt(D), so its score is t_j in log2 units. The first key tile sets the
+    reference (t = 10); a later tile sits at t = 14 (probabilities 16: a tile sum of 512 per lane trips the
+    sum guard of the D = 64 fused pass, but the exact rule leaves the reference), another at t = 30 (the
+    reference must rise), the rest below. Fused (no workspace), fused with the key split and stepwise runs
+    against the oracle on the same bf16 values."""
+    rng = np.random.default_rng(70 + d)
+    B, H, S, cp = 1, 2, 4096, 2
+    c = math.log2(math.e) / math.sqrt(d)
+    u = rng.standard_normal(d)
+    u_b = torch.from_numpy(u.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    t = np.full(S, 6.0)
+    t[:64] = 10.0
+    t[640:704] = 14.0
+    t[1500:1600] = 30.0
+    t[3000:3050] = -40.0
+    t += rng.uniform(-0.5, 0.5, S)
+    q = np.broadcast_to(u_b, (B, H, S, d)).copy()
+    k = (t[:, None] / (c * float(u_b @ u_b))) * u_b[None, :]
+    k = np.broadcast_to(k, (B, H, S, d)).copy()
+    v = rng.standard_normal((B, H, S, d))
+    dev = {n: torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).cuda() for n, x in (("q", q), ("k", k),
+                                                                                               ("v", v))}
+    host = {n: dev[n].double().cpu().numpy() for n in dev}
+    w = small_workload("rescale_paths", "bf16", B, H, d, S, cp, "zigzag", True, seed=0)
+    for rank in range(cp):
+        ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], S, cp, oracle.ZIGZAG, rank, True)
+        for flags in (cpr.RUN_FUSED, SPLIT, cpr.RUN_STEPWISE):
+            o, lse, _ = run_rank(w, dev, rank, flags)
+            compare(o, lse, ro, rl, "bf16", f"structured scores D={d} rank {rank} flags {flags}")
