@@ -31,7 +31,9 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X published dense bf16 MFMA peak
 PEAK_F32_TFLOPS = 157.3      # MI355X published fp32 vector peak
 PEAK_HBM_GBS = 8000.0        # MI355X published HBM3E bandwidth
-KERNEL_SRC = os.path.join(ROOT, "context_ring_attention_zigzag_amd", "csrc", "attn_bf16.hip")
+# the attention kernel and every header it is compiled from
+KERNEL_SRCS = [os.path.join(ROOT, "context_ring_attention_zigzag_amd", "csrc", f)
+               for f in ("attn_bf16.hip", "tile_class.h", "mfma_util.h", "common.h")]
 KERNEL_NAME = "attn_bf16_kernel"
 
 
@@ -46,8 +48,12 @@ def allowed_pairs(w, s_pad: int, lq: int, q_pos, k_pos_all) -> int:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix over the attention kernel's sources, in a fixed order."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def field_from_profile(workload: str, kind: str, field: str):
@@ -389,7 +395,8 @@ def main():
                 "kernel": (KERNEL_NAME if kv_split == 1 else f"{KERNEL_NAME} (keys split {kv_split} ways) + "
                            "merge_finalize_kernel") if w.dtype == "bf16" else "attn_f32_kernel",
                 "kernel_ms": round(kernel_ms, 4), "flop_per_launch": flop,
-                "mfma_busy_frac": mfma_busy_from_profile(w.name) if kv_split == 1 else None}
+                "mfma_busy_frac": mfma_busy_from_profile(w.name) if kv_split == 1 else None,
+                "kernel_source_sha256_16": kernel_hash()}
 
     state_kernels = measure_state_kernels(cpr, torch, w.B, w.H, ri.lq, w.D, tdt, stream, q_local=ri.q_local,
                                           q_pos=ri.q_pos)
