@@ -72,7 +72,7 @@ struct BCfg {
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
   if constexpr (D == 128) {
-    return c ^ ((((r >> 3) & 1) << 3) | ((r & 3) << 1) | ((r >> 2) & 1));
+    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
   } else {
     const int k = (r >> 1) & 7;
     return c ^ (((k & 1) << 2) | (k >> 1));
@@ -778,32 +778,49 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
         }
       };
 
-      // role A: P(k) = 2^(S(k) c - lse2(k)), masked; to LDS for role B, bf16 kept for dV(k)
+      // role A: P(k) = 2^(S(k) c - lse2(k)), masked; to LDS for role B, bf16 kept for dV(k).
+      // Lane: key ql, queries 8 * i + 4 * hh + jj of the tile (element 4 * i + jj). The lse2 reads
+      // (and the window reads of a masked tile) go out together before the first exponential, so
+      // their latencies overlap; the P stores stay spread over the phase, one per group of four,
+      // so that they do not arrive at the LDS as one burst beside role B's operand reads.
       auto a_valu = [&](int k) __attribute__((always_inline)) {
         const int slot = k % 3;
         const int e = __builtin_amdgcn_readfirstlane((int)klist[k / group]);
-        // lane: key ql, queries 8 * i + 4 * hh + jj of the tile (element 4 * i + jj)
+        float4 l2[4];
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) l2[i] = *reinterpret_cast<const float4*>(&l2_lds[slot][8 * i + 4 * hh]);
         float p[16];
-        const int remq = a.Lq - (seg0 + (e & 0x7fff)) * kT - 4 * hh;
+        if (e & 0x8000) {
+          int4 w[8];
   #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float4 l2 = *reinterpret_cast<const float4*>(&l2_lds[slot][8 * i + 4 * hh]);
-          const float l2v[4] = {l2.x, l2.y, l2.z, l2.w};
-          bool ok[4] = {true, true, true, true};
-          if (e & 0x8000) {
-            const int4 w0 = *reinterpret_cast<const int4*>(&qw_lds[slot][8 * i + 4 * hh]);
-            const int4 w1 = *reinterpret_cast<const int4*>(&qw_lds[slot][8 * i + 4 * hh + 2]);
-            const int lo[4] = {w0.x, w0.z, w1.x, w1.z};
-            const int hi[4] = {w0.y, w0.w, w1.y, w1.w};
-  #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) ok[jj] = 8 * i + jj < remq && kp >= lo[jj] && kp <= hi[jj];
+          for (int i = 0; i < 4; ++i) {
+            w[2 * i] = *reinterpret_cast<const int4*>(&qw_lds[slot][8 * i + 4 * hh]);
+            w[2 * i + 1] = *reinterpret_cast<const int4*>(&qw_lds[slot][8 * i + 4 * hh + 2]);
           }
+          const int remq = a.Lq - (seg0 + (e & 0x7fff)) * kT - 4 * hh;
   #pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const float e2 = __builtin_amdgcn_exp2f(fmaf(sx[4 * i + jj], c2, -l2v[jj]));
-            p[4 * i + jj] = ok[jj] ? e2 : 0.f;
+          for (int i = 0; i < 4; ++i) {
+            const float l2v[4] = {l2[i].x, l2[i].y, l2[i].z, l2[i].w};
+            const int lo[4] = {w[2 * i].x, w[2 * i].z, w[2 * i + 1].x, w[2 * i + 1].z};
+            const int hi[4] = {w[2 * i].y, w[2 * i].w, w[2 * i + 1].y, w[2 * i + 1].w};
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const bool ok = 8 * i + jj < remq && kp >= lo[jj] && kp <= hi[jj];
+              const float e2 = __builtin_amdgcn_exp2f(fmaf(sx[4 * i + jj], c2, -l2v[jj]));
+              p[4 * i + jj] = ok ? e2 : 0.f;
+            }
+            p_lds[pair][i * 64 + lane] = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+            __builtin_amdgcn_sched_barrier(0);
           }
-          p_lds[pair][i * 64 + lane] = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+        } else {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float l2v[4] = {l2[i].x, l2[i].y, l2[i].z, l2[i].w};
+  #pragma unroll
+            for (int jj = 0; jj < 4; ++jj) p[4 * i + jj] = __builtin_amdgcn_exp2f(fmaf(sx[4 * i + jj], c2, -l2v[jj]));
+            p_lds[pair][i * 64 + lane] = make_float4(p[4 * i], p[4 * i + 1], p[4 * i + 2], p[4 * i + 3]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
         bx0 = pack_chunk(p, 0);
         bx1 = pack_chunk(p, 1);
