@@ -49,8 +49,13 @@ class CprView(ctypes.Structure):
 
 
 class CprAttnExt(ctypes.Structure):
-    """cpr_attn_ext: K/V head count and optional per-query key-position window."""
-    _fields_ = [("H_kv", ctypes.c_int32), ("kw_lo", ctypes.c_void_p), ("kw_hi", ctypes.c_void_p)]
+    """cpr_attn_ext: K/V head count, optional per-query key-position window, and the first/last-hop flags and
+    outputs read by cp_ring_attn_step_ex."""
+    _fields_ = [("H_kv", ctypes.c_int32), ("kw_lo", ctypes.c_void_p), ("kw_hi", ctypes.c_void_p),
+                ("step_flags", ctypes.c_int32), ("o_out", ctypes.c_void_p), ("lse_out", ctypes.c_void_p)]
+
+
+STEP_FIRST, STEP_LAST = 1, 2   # CPR_STEP_FIRST, CPR_STEP_LAST
 
 
 _lib = None
@@ -167,11 +172,19 @@ def _ext(q, k, kw_lo, kw_hi):
 
 
 def cp_ring_attn_step(q, q_pos, k, v, kv_pos, causal: bool, softmax_scale: float, o_acc, m, l, stream=None,
-                      kw_lo=None, kw_hi=None):
-    """One ring step; k and v may have fewer heads than q (grouped-query attention)."""
+                      kw_lo=None, kw_hi=None, first: bool = False, last: bool = False, o_out=None, lse_out=None):
+    """One ring step; k and v may have fewer heads than q (grouped-query attention). first: start from the
+    empty state (o_acc, m, l not read); last: write o_out (and lse_out) instead of the state."""
     B, H, Lq, D = q.shape
     qv, kv, vv = view(q), view(k), view(v)
     ext = _ext(q, k, kw_lo, kw_hi)
+    flags = (STEP_FIRST if first else 0) | (STEP_LAST if last else 0)
+    if flags:
+        if ext is None:
+            ext = CprAttnExt(k.shape[1], None, None)
+        ext.step_flags = flags
+        ext.o_out = None if o_out is None else o_out.data_ptr()
+        ext.lse_out = None if lse_out is None else lse_out.data_ptr()
     _check(load().cp_ring_attn_step_ex(dtype_code(q), B, H, D, ctypes.byref(qv), Lq, _ptr(q_pos), ctypes.byref(kv),
                                        ctypes.byref(vv), k.shape[2], _ptr(kv_pos), int(bool(causal)),
                                        float(softmax_scale), None if ext is None else ctypes.byref(ext), _ptr(o_acc),

@@ -235,13 +235,26 @@ cpr_status cp_ring_attn_step_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, 
                                 const int32_t* kv_pos, int32_t causal, float softmax_scale, const cpr_attn_ext* ext,
                                 float* o_acc, float* m, float* l, void* stream) {
   TRY(validate_attn(dtype, B, H, D, q, Lq, q_pos, k, v, Lk, kv_pos, ext));
-  TRY(check_state(0, o_acc, m, l));
+  const int32_t sf = ext ? ext->step_flags : 0;
+  if (sf & ~(CPR_STEP_FIRST | CPR_STEP_LAST)) return fail(CPR_EINVAL, "unknown step_flags %d", sf);
+  const bool first = (sf & CPR_STEP_FIRST) != 0, last = (sf & CPR_STEP_LAST) != 0;
+  if (!(first && last)) TRY(check_state(0, o_acc, m, l));   // the state is read, written or both
+  if (last) {
+    if (!ext->o_out) return fail(CPR_EINVAL, "CPR_STEP_LAST needs o_out");
+    if (!aligned(ext->o_out, 16)) return fail(CPR_EINVAL, "o_out must be 16-byte aligned");
+    if (ext->lse_out && !aligned(ext->lse_out, 4)) return fail(CPR_EINVAL, "lse_out must be 4-byte aligned");
+  }
   if (!(softmax_scale == softmax_scale) || isinf(softmax_scale))
     return fail(CPR_EINVAL, "softmax_scale must be finite");
   AttnArgs a = make_args(dtype, B, H, D, q, Lq, q_pos, k, v, Lk, kv_pos, causal, softmax_scale, ext);
   a.nblocks = 1; a.rank = 0; a.cp = 1;
   a.o_acc = o_acc; a.m = m; a.l = l;
-  a.load_state = 1; a.finalize = 0;
+  a.load_state = first ? 0 : 1;
+  a.finalize = last ? 1 : 0;
+  if (last) {
+    a.o_out = ext->o_out;
+    a.lse = ext->lse_out;
+  }
   return launched(launch_attn(dtype, a, static_cast<hipStream_t>(stream)),
                   static_cast<hipStream_t>(stream), "cp_ring_attn_step");
 }
@@ -359,17 +372,19 @@ cpr_status cp_ring_attn_run_ex(int32_t dtype, int32_t B, int32_t H, int32_t D, i
   float* o_acc = reinterpret_cast<float*>(w);
   float* m = reinterpret_cast<float*>(w + round256(rows * D * sizeof(float)));
   float* l = reinterpret_cast<float*>(w + round256(rows * D * sizeof(float)) + round256(rows * sizeof(float)));
-  hipError_t e = launch_state_init((int64_t)rows, D, o_acc, m, l, st);
-  if (e != hipSuccess) return hip_status(e, "cp_ring_attn_run(init)");
+  // the per-hop calls: the first step starts from the empty state, the last
+  // one writes the output (cp_ring_attn_step_ex with CPR_STEP_FIRST, CPR_STEP_LAST)
   a.o_acc = o_acc; a.m = m; a.l = l;
-  a.load_state = 1; a.finalize = 0; a.nblocks = 1; a.cp = cp_size;
+  a.o_out = o_out; a.lse = lse_out;
+  a.nblocks = 1; a.cp = cp_size;
   for (int t = 0; t < cp_size; ++t) {
     a.rank = ((rank - t) % cp_size + cp_size) % cp_size;   // block held after t hops
-    e = launch_attn(dtype, a, st);
+    a.load_state = t > 0 ? 1 : 0;
+    a.finalize = t == cp_size - 1 ? 1 : 0;
+    const hipError_t e = launch_attn(dtype, a, st);
     if (e != hipSuccess) return hip_status(e, "cp_ring_attn_run(step)");
   }
-  return launched(launch_finalize(dtype == CPR_BF16, (int64_t)rows, D, o_acc, m, l, o_out, lse_out, st),
-                  st, "cp_ring_attn_run(finalize)");
+  return launched(hipSuccess, st, "cp_ring_attn_run(stepwise)");
 }
 
 }  // extern "C"

@@ -81,7 +81,8 @@ typedef enum {
 /* Flags for cp_ring_attn_run. */
 enum {
   CPR_RUN_FUSED = 0,    /* one launch walks every ring block; optional workspace */
-  CPR_RUN_STEPWISE = 1  /* init, cp calls of the step kernel, finalize; needs the workspace */
+  CPR_RUN_STEPWISE = 1  /* cp calls of the step kernel, the first from the empty state and the last
+                           writing the output (CPR_STEP_FIRST, CPR_STEP_LAST); needs the workspace */
 };
 
 /* Strided [B, H, L, D] view; strides in elements, D contiguous. */
@@ -243,7 +244,32 @@ typedef struct cpr_attn_ext {
   int32_t H_kv;
   const int32_t* kw_lo;
   const int32_t* kw_hi;
+  /* Read by cp_ring_attn_step_ex only (ignored by every other entry point):
+   * step_flags, a combination of CPR_STEP_FIRST and CPR_STEP_LAST (0: an
+   * ordinary step), and the outputs o_out, lse_out of a CPR_STEP_LAST step. */
+  int32_t step_flags;
+  void* o_out;
+  float* lse_out;
 } cpr_attn_ext;
+
+/*
+ * The first and the last hop of a ring, for cp_ring_attn_step_ex. The running
+ * state starts empty and is normalised once after the last block
+ * ("Sequence Parallelism and Ring Attention", "Technical insight"); these
+ * flags fold those two ends into the steps themselves:
+ *   CPR_STEP_FIRST  o_acc, m, l are not read on entry: the step starts from
+ *                   O = 0, m = -inf, l = 0, so no cp_ring_attn_init is needed.
+ *   CPR_STEP_LAST   o_acc, m, l are not written: the step writes
+ *                   o_out = O / l [B,H,Lq,D] in the dtype of q (16-byte
+ *                   aligned, contiguous) and, when lse_out is not NULL,
+ *                   lse_out = m + ln l [B,H,Lq] float32, as
+ *                   cp_ring_attn_finalize would after an ordinary step.
+ * With both flags the state pointers may be NULL (one block is the whole
+ * ring). o_out and lse_out must not alias q, k, v or the state. Unknown bits,
+ * or CPR_STEP_LAST with o_out NULL, return CPR_EINVAL.
+ */
+#define CPR_STEP_FIRST 1
+#define CPR_STEP_LAST 2
 
 /* cp_ring_attn_step with the extensions above; k and v are [B, H_kv, Lk, D]. */
 cpr_status cp_ring_attn_step_ex(int32_t dtype, int32_t B, int32_t H, int32_t D,

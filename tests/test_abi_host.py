@@ -242,6 +242,24 @@ def test_extension_validation(lib):
 
 
 
+def test_step_flags_validation(lib):
+    """cp_ring_attn_step_ex checks its first/last-hop flags and their outputs before launching anything."""
+    q, k, v = view(), view(), view()
+    p = fake_ptr()
+
+    def step(ext, state=p):
+        return lib.cp_ring_attn_step_ex(cpr.BF16, 1, 2, 128, ctypes.byref(q), 64, p, ctypes.byref(k), ctypes.byref(v),
+                                        64, p, 1, 0.0, ctypes.byref(ext), state, state, state, None)
+
+    assert step(cpr.CprAttnExt(2, None, None, 4)) == cpr.EINVAL                   # unknown bit
+    assert step(cpr.CprAttnExt(2, None, None, cpr.STEP_LAST)) == cpr.EINVAL       # no o_out
+    assert step(cpr.CprAttnExt(2, None, None, cpr.STEP_LAST, fake_ptr(0x100008))) == cpr.EINVAL   # misaligned
+    assert step(cpr.CprAttnExt(2, None, None, cpr.STEP_LAST, p, fake_ptr(0x100002))) == cpr.EINVAL
+    # the state is needed unless both flags are set
+    assert step(cpr.CprAttnExt(2, None, None, cpr.STEP_FIRST), state=None) == cpr.EINVAL
+    assert step(cpr.CprAttnExt(2, None, None, cpr.STEP_LAST, p), state=None) == cpr.EINVAL
+
+
 def test_bwd_workspace_size(lib):
     ws = lib.cp_ring_attn_bwd_workspace_size(2, 16, 8192)
     assert ws >= 2 * 16 * 8192 * 8 + 8192 * 8 and ws % 256 == 0

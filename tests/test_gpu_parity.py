@@ -8,6 +8,7 @@ the benchmark times, and the 1M-token share is also checked on every row
 against the K = 0 closed form (LSE = ln #allowed, O = mean of allowed V).
 """
 
+import ctypes
 import math
 import zlib
 
@@ -317,6 +318,64 @@ def test_step_states_match_ring_emulation(dtype, D):
         assert np.array_equal(np.isneginf(gm), np.isneginf(rm))
         fin = np.isfinite(rm)
         assert np.abs(gm[fin] - rm[fin]).max() <= 1e-4
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_step_first_and_last_flags(dtype, D):
+    """Per-hop calls with CPR_STEP_FIRST and CPR_STEP_LAST against the oracle's ring states: the first step
+    ignores a NaN-filled state, the last writes O and LSE itself and leaves the state alone, and one block with
+    both flags (no state at all) is that block's attention."""
+    w = small_workload("stepflags", dtype, 1, 2, D, 700, 4, "zigzag", True, seed=12)
+    dev, host = natural_inputs(w)
+    r = 1
+    ri = di.prepare_rank(dev["q"], dev["k"], dev["v"], w.S, w.cp, cpr.ZIGZAG, r)
+    lq = ri.lq
+    o_acc = torch.full((w.B, w.H, lq, D), float("nan"), device="cuda")
+    m = torch.full((w.B, w.H, lq), float("nan"), device="cuda")
+    l = torch.full_like(m, float("nan"))
+    tok, pos = oracle.layout(w.S, w.cp, oracle.ZIGZAG)
+    qr = np.zeros((w.B, w.H, len(tok), D))
+    kr, vr = np.zeros_like(qr), np.zeros_like(qr)
+    real = tok < w.S
+    for x, y in ((qr, "q"), (kr, "k"), (vr, "v")):
+        x[:, :, real] = host[y][:, :, tok[real]]
+    sl = slice(r * lq, (r + 1) * lq)
+    _, states = oracle.ring_emulation(qr[:, :, sl], kr, vr, pos[sl], pos, w.cp, r, True, keep_states=True)
+    o_out = torch.empty(w.B, w.H, lq, D, dtype=TDT[dtype], device="cuda")
+    lse = torch.empty(w.B, w.H, lq, device="cuda")
+
+    def block(t):
+        bs = slice(oracle.ring_source(r, t, w.cp) * lq, (oracle.ring_source(r, t, w.cp) + 1) * lq)
+        return ri.k_ring[:, :, bs], ri.v_ring[:, :, bs], ri.ring_pos[bs]
+
+    for t in range(w.cp):
+        k, v, kp = block(t)
+        last = t == w.cp - 1
+        if last:
+            before = [x.clone() for x in (o_acc, m, l)]
+        cpr.cp_ring_attn_step(ri.q_local, ri.q_pos, k, v, kp, True, 0.0, o_acc, m, l, first=t == 0, last=last,
+                              o_out=o_out, lse_out=lse)
+        torch.cuda.synchronize()
+        if t == 0:
+            go, gl = oracle.finalize((o_acc.cpu().numpy(), m.cpu().numpy(), l.cpu().numpy()))
+            ro, rl = oracle.finalize(states[0])
+            compare(go, gl, ro, rl, dtype, "first step (NaN state on entry)")
+    assert all(torch.equal(a, b) for a, b in zip(before, (o_acc, m, l))), "the last step wrote the state"
+    ro, rl = oracle.finalize(states[w.cp - 1])
+    compare(o_out.float().cpu().numpy(), lse.cpu().numpy(), ro, rl, dtype, "last step output")
+    # one block, both flags, no state
+    k, v, kp = block(0)
+    o1 = torch.empty_like(o_out)
+    l1 = torch.empty_like(lse)
+    ext = cpr.CprAttnExt(w.H, None, None, cpr.STEP_FIRST | cpr.STEP_LAST, o1.data_ptr(), l1.data_ptr())
+    qv, kv, vv = cpr.view(ri.q_local), cpr.view(k), cpr.view(v)
+    st = cpr.load().cp_ring_attn_step_ex(cpr.dtype_code(ri.q_local), w.B, w.H, D, ctypes.byref(qv), lq,
+                                         ri.q_pos.data_ptr(), ctypes.byref(kv), ctypes.byref(vv), lq, kp.data_ptr(),
+                                         1, 0.0, ctypes.byref(ext), None, None, None, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    ro, rl = oracle.finalize(states[0])
+    compare(o1.float().cpu().numpy(), l1.cpu().numpy(), ro, rl, dtype, "one block, both flags")
 
 
 # ---------------------------------------------------- state kernels alone
