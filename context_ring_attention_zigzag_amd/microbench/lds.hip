@@ -98,6 +98,58 @@ __global__ void __launch_bounds__(512) lds_rate(uint64_t* out, int* sink, int nw
   sink[blockIdx.x * 512 + tid] = acc;
 }
 
+// ---- the same reads with all 16 in flight before any is used: one asm statement consumes them, so the
+// compiler waits once per group instead of in step with the reads
+template <int MODE>
+__global__ void __launch_bounds__(512) lds_rate16(uint64_t* out, int* sink, int nwaves) {
+  __shared__ __attribute__((aligned(16))) short lds[32768];   // 64 KB
+  extern __shared__ char reserve[];
+  if (threadIdx.x == 0) reserve[0] = 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 32768; i += blockDim.x) lds[i] = (short)i;
+  __syncthreads();
+  int acc = 0;
+  uint64_t t0 = 0, t1 = 0;
+  if (wave < nwaves) {
+    const uint32_t base = (uint32_t)wave * 8192u;
+    uint32_t off;
+    if constexpr (MODE == 0) {
+      off = base + (uint32_t)(lane & 15) * 16u + (uint32_t)(lane >> 4) * 256u;
+    } else {
+      const int r = 4 * (lane >> 5) + ((lane & 15) >> 2);
+      off = base + (uint32_t)r * 256u + (uint32_t)(((r & 3) * 4 + 2 * ((lane >> 4) & 1)) * 16) + (uint32_t)(lane & 3) * 8u;
+    }
+    t0 = __builtin_amdgcn_s_memtime();
+    for (int it = 0; it < kIters; ++it) {
+      if constexpr (MODE == 0) {
+        i32x4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          asm volatile("" ::: "memory");
+          v[u] = *reinterpret_cast<const i32x4*>((const char*)lds + off + (uint32_t)(u & 7) * 1024u - ((u & 7) == 7 ? 1024u : 0u));
+        }
+        asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
+                     "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+        acc += v[0].x + it;
+      } else {
+        s16x4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          asm volatile("" ::: "memory");
+          v[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)((const char*)lds + off + (uint32_t)(u & 3) * 2048u));
+        }
+        asm volatile("" ::"v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]),
+                     "v"(v[8]), "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+        acc += (int)v[0][0] + it;
+      }
+    }
+    t1 = __builtin_amdgcn_s_memtime();
+  }
+  __syncthreads();
+  if (lane == 0 && wave < nwaves) out[blockIdx.x * 8 + wave] = t1 - t0;
+  sink[blockIdx.x * 512 + tid] = acc;
+}
+
 // ---- direct-to-LDS load issue cost: NL loads per wave, timed from the first issue to the last
 template <int NL>
 __global__ void __launch_bounds__(512) dma_issue(const char* src, uint64_t* out, int* sink, int nwaves) {
@@ -186,6 +238,21 @@ int main() {
       const double bytes = (double)kIters * 16 * bytes_per_op[mode];
       printf("%-38s waves %d: %5.1f cycles per instruction per wave, %6.1f B/cycle per wave, %6.1f per CU\n",
              names[mode], nw, cyc / (kIters * 16.0), bytes / cyc, nw * bytes / cyc);
+    }
+  const char* names16[2] = {"ds_read_b128 rows, 16 in flight", "ds_read_b64_tr_b16, 16 in flight"};
+  for (int mode = 0; mode < 2; ++mode)
+    for (int nw : {1, 4, 8}) {
+      for (int rep = 0; rep < 2; ++rep) {
+        if (mode == 0) hipLaunchKernelGGL(lds_rate16<0>, dim3(nblk), dim3(512), kReserve, 0, out, sink, nw);
+        else hipLaunchKernelGGL(lds_rate16<1>, dim3(nblk), dim3(512), kReserve, 0, out, sink, nw);
+        CHECK(hipGetLastError());
+        CHECK(hipDeviceSynchronize());
+      }
+      CHECK(hipMemcpy(h.data(), out, h.size() * sizeof(uint64_t), hipMemcpyDeviceToHost));
+      const double cyc = mean_nonzero(h, nblk, nw);
+      const double bytes = (double)kIters * 16 * (mode == 0 ? 1024 : 512);
+      printf("%-38s waves %d: %5.1f cycles per instruction per wave, %6.1f B/cycle per wave, %6.1f per CU\n",
+             names16[mode], nw, cyc / (kIters * 16.0), bytes / cyc, nw * bytes / cyc);
     }
   for (int nl : {1, 2, 4, 8})
     for (int nw : {1, 4, 8}) {
