@@ -95,21 +95,24 @@ __device__ __forceinline__ uint32_t dma_off(unsigned sidx, int64_t sl) {
 }
 
 // A-operand fragments of a tile: row ql, logical chunk 2 * kk + hh (8 columns
-// of the contraction dim).
+// of the contraction dim). The offsets are kept in bytes, so that a read is
+// the lane register plus the array's address as an immediate, with no vector
+// instruction in front of it (in a matrix phase those would wait behind the
+// other wave's vector stream on the same SIMD).
 template <int D>
 struct RowFrags {
   int off[BCfg<D>::kKSteps];
   __device__ __forceinline__ void init(int ql, int hh) {
 #pragma unroll
-    for (int kk = 0; kk < BCfg<D>::kKSteps; ++kk) off[kk] = tile_off<D>(ql, 16 * kk + 8 * hh);
+    for (int kk = 0; kk < BCfg<D>::kKSteps; ++kk) off[kk] = 2 * tile_off<D>(ql, 16 * kk + 8 * hh);
   }
   __device__ __forceinline__ bf16x8 get(const __bf16* tile, int kk) const {
-    return *reinterpret_cast<const bf16x8*>(tile + off[kk]);
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(tile) + off[kk]);
   }
   // move every offset by d elements (to another tile buffer of the same array)
   __device__ __forceinline__ void shift(int d) {
 #pragma unroll
-    for (int kk = 0; kk < BCfg<D>::kKSteps; ++kk) off[kk] += d;
+    for (int kk = 0; kk < BCfg<D>::kKSteps; ++kk) off[kk] += 2 * d;
   }
 };
 
@@ -121,27 +124,28 @@ struct RowFrags {
 // Row r + 16 has the swizzle of row r, so chunk c = 1 sits 16 rows further.
 template <int D>
 struct TrFrags {
-  int off[2][BCfg<D>::kDTiles];
+  int off[2][BCfg<D>::kDTiles];   // bytes, as in RowFrags
   __device__ __forceinline__ void init(int lane) {
     const int r = 4 * (lane >> 5) + ((lane & 15) >> 2);
     const int col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 #pragma unroll
     for (int dt = 0; dt < BCfg<D>::kDTiles; ++dt) {
-      off[0][dt] = tile_off<D>(r, 32 * dt + col);
-      off[1][dt] = tile_off<D>(r + 8, 32 * dt + col);
+      off[0][dt] = 2 * tile_off<D>(r, 32 * dt + col);
+      off[1][dt] = 2 * tile_off<D>(r + 8, 32 * dt + col);
     }
   }
   __device__ __forceinline__ bf16x8 get(const __bf16* tile, int c, int dt) const {
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off[0][dt] + 16 * c * D));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + off[1][dt] + 16 * c * D));
+    const char* t = reinterpret_cast<const char*>(tile);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + off[0][dt] + 32 * c * D));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(t + off[1][dt] + 32 * c * D));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
   // see RowFrags::shift
   __device__ __forceinline__ void shift(int d) {
 #pragma unroll
     for (int dt = 0; dt < BCfg<D>::kDTiles; ++dt) {
-      off[0][dt] += d;
-      off[1][dt] += d;
+      off[0][dt] += 2 * d;
+      off[1][dt] += 2 * d;
     }
   }
 };
