@@ -444,11 +444,13 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
         if (wave == 0) dma_b32(make_rsrc(posb + r0, rows * 4u), (uint32_t)lane * 4u, lds_addr(&pos_lds[slot][0]));
       };
 
-      issue(klist[0] & 0x7fff, 0);
-      for (int u = 0; u < nk; ++u) {
+      // one kept tile u in buffer `slot`; the buffer index is a compile-time constant of each copy
+      // of the body (the loop below takes two tiles per turn), so that every operand read is the
+      // lane's offset plus the buffer's address as an immediate
+      auto tile = [&](int u, auto slot_c) __attribute__((always_inline)) {
+        constexpr int slot = decltype(slot_c)::value;
         const int e = __builtin_amdgcn_readfirstlane((int)klist[u]);
         const int en = __builtin_amdgcn_readfirstlane((int)klist[u + 1]);
-        const int slot = u & 1;
         vm_wait<0>();
         bar();   // tile u is in LDS; every wave is done with buffer (u + 1) & 1
         if (u + 1 < nk) issue(en & 0x7fff, slot ^ 1);
@@ -496,6 +498,12 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
               const int dt = m % C::kDTiles;
               dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, m < C::kDTiles ? d0 : d1, dqt[dt], 0, 0, 0);
             });
+      };
+
+      issue(klist[0] & 0x7fff, 0);
+      for (int u = 0; u < nk; u += 2) {
+        tile(u, ic<0>{});
+        if (u + 1 < nk) tile(u + 1, ic<1>{});
       }
     }
   }
