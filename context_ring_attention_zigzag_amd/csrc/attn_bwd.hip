@@ -19,9 +19,10 @@
 //    and Dvec, and the positions into a per-query allowed window {lo, hi};
 //  * every streamed tile is 32 rows, stored once in LDS, row-major with a
 //    16-byte-chunk XOR swizzle chosen so that both access patterns are free of
-//    bank conflicts: the row reads of an A operand (16 lanes, 16 rows, one
-//    chunk) and the transposed reads (ds_read_b64_tr_b16: 16 lanes, 4 rows, two
-//    chunks) that give the tile's transpose as an A operand;
+//    bank conflicts: the row reads of an A operand (an LDS pass serves 16
+//    lanes: 16 rows at one chunk) and the transposed reads (ds_read_b64_tr_b16,
+//    a pass serves 32 lanes: 4 aligned rows at 4 aligned chunks) that give the
+//    tile's transpose as an A operand;
 //  * the dQ kernel: a workgroup owns 128 queries of one (b, h), each wave 32 of
 //    them with Q and dO resident in VGPRs in the B-operand layout of
 //    v_mfma_f32_32x32x16_bf16. Keys stream through LDS in tiles of 32 with
@@ -65,10 +66,12 @@ struct BCfg {
 };
 
 // Physical 16-byte chunk of logical chunk c in row r of a streamed tile. The
-// XOR pattern is a permutation of the row's low bits: bits (r3, r1, r0, r2) for
-// D = 128; for D = 64, whose rows are half a bank sweep, a bit rotation of
-// (r >> 1) & 7. Either way 16 consecutive rows at one chunk hit 16 distinct
-// bank groups, and 4 consecutive rows at an aligned chunk pair hit 8.
+// XOR value is a permutation of the row's low bits: bits (r1, r0, r3, r2) for
+// D = 128, whose rows are one 256-byte bank sweep each, so that the two low row
+// bits pick the chunk quad; for D = 64, whose rows are half a sweep, a bit
+// rotation of (r >> 1) & 7. Either way the 16 rows of a row-read pass at one
+// chunk hit 16 distinct 16-byte bank groups, and so do the 4 aligned rows x 4
+// aligned chunks of a 32-lane transposed pass.
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
   if constexpr (D == 128) {
@@ -119,8 +122,9 @@ struct RowFrags {
 // A-operand fragments of the transposed tile through two transposed reads:
 // lane (column d = 32 * dt + lane % 32, half hh) gets rows 16c + 4hh + {0..3}
 // and 16c + 8 + 4hh + {0..3}, the rows whose values a B operand packed from an
-// accumulator chunk c holds for k = 8 * hh + {0..7}. 16-lane group g reads row
-// 4 * hh + (gi >> 2) of its 4-row group, 4 columns at 16 * (g & 1) + 4 * (gi & 3).
+// accumulator chunk c holds for k = 8 * hh + {0..7}. Lane l reads row
+// 4 * hh + ((l % 16) >> 2) and the 4 columns at 16 * ((l / 16) & 1) + 4 * (l % 4)
+// of its d tile.
 // Row r + 16 has the swizzle of row r, so chunk c = 1 sits 16 rows further.
 template <int D>
 struct TrFrags {
