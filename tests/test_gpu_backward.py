@@ -63,7 +63,8 @@ def check(got, ref, dtype, what, zero_rows=None):
 class Case:
     """Seeded natural-order inputs of one backward parity case, on host and device."""
 
-    def __init__(self, dtype, B, H, H_kv, D, S, cp, layout, causal, seed, docs=None, scale=1.0):
+    def __init__(self, dtype, B, H, H_kv, D, S, cp, layout, causal, seed, docs=None, scale=1.0, windows=None):
+        """docs: packed-document lengths (per-query windows from them); windows: (lo, hi) per natural position."""
         rng = np.random.default_rng(seed)
         self.dtype, self.B, self.H, self.H_kv, self.D, self.S, self.cp = dtype, B, H, H_kv, D, S, cp
         self.causal = causal
@@ -77,6 +78,8 @@ class Case:
         self.lo_nat = self.hi_nat = None
         if docs is not None:
             self.lo_nat, self.hi_nat = packed_windows(docs, causal)
+        if windows is not None:
+            self.lo_nat, self.hi_nat = (np.asarray(x, dtype=np.int64) for x in windows)
 
     def host_gather(self, x, idx):
         out = np.zeros(x.shape[:2] + (len(idx), x.shape[-1]))
@@ -170,6 +173,24 @@ def test_bwd_packed_documents(dtype):
     docs = [300, 5, 700, 1, 250, 44] if dtype == "bf16" else [100, 5, 77, 1, 50]
     c = Case(dtype, 1, 4, 2, 128 if dtype == "bf16" else 64, sum(docs), 4, "striped", True, seed=306, docs=docs)
     run_case(c, (0, 3), f"{dtype}_docs")
+
+
+@pytest.mark.parametrize("dtype,d,S,cp,layout,causal,half,empty_every", [
+    ("bf16", 128, 1500, 4, "zigzag", True, 100, 7),
+    ("bf16", 64, 1200, 3, "striped", False, 80, 11),
+    ("f32", 64, 500, 2, "zigzag", True, 50, 5),
+])
+def test_bwd_sliding_windows_with_empty_windows(dtype, d, S, cp, layout, causal, half, empty_every):
+    """Per-query key windows of a sliding-window model: [t - half, t] causal or [t - half, t + half]
+    bidirectional, with every empty_every-th query given an empty window (hi < lo). Those queries have
+    LSE = -inf in the forward and must get dQ = 0; keys that no window reaches must get dK = dV = 0."""
+    t = np.arange(S)
+    lo = np.maximum(t - half, 0)
+    hi = t if causal else t + half
+    hi = np.where(t % empty_every == 3, lo - 1, hi)
+    c = Case(dtype, 1, 2, 2, d, S, cp, layout, causal, seed=320 + d + cp, windows=(lo, hi))
+    run_case(c, range(cp), f"{dtype}_window_{layout}_d{d}")
+    assert c.zero_rows[0].any(), "some query of the last rank has an empty window"
 
 
 @pytest.mark.parametrize("d", [128, 64])

@@ -268,20 +268,26 @@ def test_mid_size_grouped_heads_documents_padded(layout):
             compare(o, lse, ro, rl, "bf16", f"mid {layout} r{r} f{flags}")
 
 
-def test_sliding_window_with_empty_windows():
-    """Causal window of 100 keys; every 7th query gets an empty window (hi < lo): O = 0, LSE = -inf there."""
-    w = small_workload("window", "bf16", 1, 2, 128, 1500, 4, "zigzag", True, seed=21)
+@pytest.mark.parametrize("dtype,D,S,cp,layout,causal,half,empty_every", [
+    ("bf16", 128, 1500, 4, "zigzag", True, 100, 7),
+    ("bf16", 64, 1200, 3, "striped", False, 80, 11),
+    ("f32", 64, 500, 2, "zigzag", True, 50, 5),
+])
+def test_sliding_window_with_empty_windows(dtype, D, S, cp, layout, causal, half, empty_every):
+    """Sliding key windows, [t - half, t] causal or [t - half, t + half] bidirectional; every empty_every-th
+    query gets an empty window (hi < lo): O = 0, LSE = -inf there."""
+    w = small_workload("window", dtype, 1, 2, D, S, cp, layout, causal, seed=21 + D + cp)
     dev, host = natural_inputs(w)
     t = np.arange(w.S)
-    lo = np.maximum(t - 100, 0).astype(np.int32)
-    hi = np.where(t % 7 == 3, lo - 1, t).astype(np.int32)
+    lo = np.maximum(t - half, 0).astype(np.int32)
+    hi = np.where(t % empty_every == 3, lo - 1, t if causal else t + half).astype(np.int32)
     for r in range(w.cp):
-        ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], w.S, w.cp, oracle.ZIGZAG, r, True,
+        ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], w.S, w.cp, ORACLE_LAYS[layout], r, causal,
                                        kw_lo_nat=lo, kw_hi_nat=hi)
         assert np.isneginf(rl).any()
         for flags in MODES:
             o, lse = run_rank_ext(w, dev["q"], dev["k"], dev["v"], r, flags, lo, hi)
-            compare(o, lse, ro, rl, "bf16", f"window r{r} f{flags}")
+            compare(o, lse, ro, rl, dtype, f"window {layout} D{D} r{r} f{flags}")
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
