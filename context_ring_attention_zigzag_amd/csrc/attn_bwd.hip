@@ -29,12 +29,13 @@
 //    direct buffer->LDS loads, double-buffered. S^T = K Q^T and dP^T = V dO^T
 //    put one query and 16 keys in each lane, so P^T and dS^T are lane-local and
 //    leave the accumulators already in the B-operand layout of
-//    dQ^T += K^T dS^T (v_cvt_pk_bf16_f32, round to nearest even); two
-//    workgroups share a CU;
+//    dQ^T += K^T dS^T (v_cvt_pk_bf16_f32, round to nearest even), whose first
+//    K^T fragments are read before the tile's vector work; two workgroups
+//    share a CU;
 //  * the dK/dV kernel: a workgroup owns 128 keys of one (b, kv head) as four
 //    pairs of waves, 32 keys per pair, and streams query tiles (Q, dO, lse2,
 //    Dvec, windows) of every query head of the grouped-query group through
-//    three LDS buffers. The two waves of a pair share a SIMD and split the work
+//    four LDS buffers. The two waves of a pair share a SIMD and split the work
 //    of each tile: role A computes S = Q K^T and P (masked) and dV^T += dO^T P
 //    with K resident; role B computes dP = dO V^T and dS = P * (dP - Dvec) with
 //    P handed over through LDS in float32, and dK^T += Q^T dS with V resident.
@@ -187,6 +188,36 @@ __device__ __forceinline__ void mfma_stream(Fetch&& fetch, Mma&& mma) {
   for (int m = 0; m < N; ++m) {
     if (m + kPf < N) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads, 0);
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  }
+}
+
+// mfma_stream whose first kPf fragments the caller has already read into fr
+// (before the barrier that opens the phase, so that the first MFMA does not
+// wait out the LDS latency)
+template <int N, int kReads, typename Fetch, typename Mma>
+__device__ __forceinline__ void mfma_stream_pre(bf16x8 (&fr)[kPf + 1], Fetch&& fetch, Mma&& mma) {
+  static_assert(N >= kPf, "the prefetched fragments belong to this stream");
+#pragma unroll
+  for (int m = 0; m < N; ++m) {
+    if (m + kPf < N) fr[(m + kPf) % (kPf + 1)] = fetch(m + kPf);
+    mma(m, fr[m % (kPf + 1)]);
+  }
+#pragma unroll
+  for (int m = 0; m < N; ++m) {
+    if (m + kPf < N) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kReads, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+  }
+}
+
+// mfma_stream_pre with side(m) called after MFMA m
+template <int N, int kReads, typename Fetch, typename Mma, typename Side>
+__device__ __forceinline__ void mfma_stream_side_pre(bf16x8 (&fr)[kPf + 1], Fetch&& fetch, Mma&& mma, Side&& side) {
+  static_assert(N >= kPf, "the prefetched fragments belong to this stream");
+#pragma unroll
+  for (int m = 0; m < N; ++m) {
+    if (m + kPf < N) fr[(m + kPf) % (kPf + 1)] = fetch(m + kPf);
+    mma(m, fr[m % (kPf + 1)]);
+    side(m);
   }
 }
 
@@ -470,6 +501,12 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
               else st = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[m >> 1], st, 0, 0, 0);
             });
 
+        // the first fragments of the dQ stream (K^T of this tile) go out now and land during the
+        // vector work below
+        bf16x8 qfr[kPf + 1];
+#pragma unroll
+        for (int m = 0; m < kPf; ++m) qfr[m] = trf.get(kl, m / C::kDTiles, m % C::kDTiles);
+
         // lane: query ql, keys 8 * i + 4 * hh + jj of the tile (element 4 * i + jj)
         float s[16], ds[16];
 #pragma unroll
@@ -496,8 +533,8 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
         const bf16x8 d0 = pack_chunk(ds, 0), d1 = pack_chunk(ds, 1);
 
         // dQ^T += K^T dS^T
-        mfma_stream<2 * C::kDTiles, 2>(
-            [&](int m) { return trf.get(kl, m / C::kDTiles, m % C::kDTiles); },
+        mfma_stream_pre<2 * C::kDTiles, 2>(
+            qfr, [&](int m) { return trf.get(kl, m / C::kDTiles, m % C::kDTiles); },
             [&](int m, const bf16x8& a) {
               const int dt = m % C::kDTiles;
               dqt[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, m < C::kDTiles ? d0 : d1, dqt[dt], 0, 0, 0);
@@ -541,14 +578,19 @@ __global__ void __launch_bounds__(kQThreads, 2) bwd_dq_kernel(BwdArgs a) {
 // (items) run in phases separated by workgroup barriers, and in every phase one
 // role works the matrix cores while the other works the vector ALU:
 //   phase 2k:   A: S(k) = Q(k) K^T, then dV^T += dO(k-1)^T P(k-1),
-//                  with the loads of item k + 1 between the MFMAs    [MFMA]
+//                  with the loads of item k + 2 between the MFMAs    [MFMA]
 //               B: dS(k-1) = P(k-1) * (dP(k-1) - Dvec(k-1))          [VALU]
 //   phase 2k+1: A: P(k) = 2^(S(k) c - lse2(k)), masked, handed to B
 //                  through LDS in float32                            [VALU]
 //               B: dP(k) = dO(k) V^T, then dK^T += Q(k-1)^T dS(k-1)  [MFMA]
-// Items rotate through three LDS buffers: phase 2k reads items k - 1 and k,
-// loads item k + 1 into the buffer of item k - 2, and role A waits for those
-// loads at the end of phase 2k + 1, one barrier before their first reader.
+// Items rotate through four LDS buffers. Phase 2k reads items k - 1 and k and
+// loads item k + 2 into the buffer of item k - 2, whose last reader was phase
+// 2k - 1; role A waits for those loads at the end of phase 2k + 1, so item
+// k + 2 is visible from phase 2k + 2 on, two phases before its first reader.
+// That slack lets each role read the first operand fragments of its next
+// matrix phase before the barrier that opens it (role A at the start of its
+// vector phase, role B at the end of its own), so that the first MFMA of a
+// phase does not wait out the LDS latency.
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int kKvOwn = 128;                   // keys per workgroup, 32 per pair
@@ -561,11 +603,12 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
   constexpr int kLoads = C::kTileLoads / 2;   // per role-A wave: two waves per tensor
   static_assert(kLoads >= 1 && C::kTileLoads % 2 == 0, "tile/waves mismatch");
 
-  __shared__ __attribute__((aligned(16))) __bf16 q_lds[3][kT * D];   // Q tiles (S A operand, Q^T reads)
-  __shared__ __attribute__((aligned(16))) __bf16 g_lds[3][kT * D];   // dO tiles (dP A operand, dO^T reads)
-  __shared__ __attribute__((aligned(16))) float l2_lds[3][64];       // lse2 of the tile's queries (32 used)
-  __shared__ __attribute__((aligned(16))) float dv_lds[3][64];       // Dvec of the tile's queries (32 used)
-  __shared__ __attribute__((aligned(16))) int2 qw_lds[3][kT];        // {lo, hi} of the tile's queries
+  constexpr int kBufs = 4;   // item buffers: loads go out two items ahead
+  __shared__ __attribute__((aligned(16))) __bf16 q_lds[kBufs][kT * D];   // Q tiles (S A operand, Q^T reads)
+  __shared__ __attribute__((aligned(16))) __bf16 g_lds[kBufs][kT * D];   // dO tiles (dP A operand, dO^T reads)
+  __shared__ __attribute__((aligned(16))) float l2_lds[kBufs][64];       // lse2 of the tile's queries (32 used)
+  __shared__ __attribute__((aligned(16))) float dv_lds[kBufs][64];       // Dvec of the tile's queries (32 used)
+  __shared__ __attribute__((aligned(16))) int2 qw_lds[kBufs][kT];        // {lo, hi} of the tile's queries
   __shared__ __attribute__((aligned(16))) float4 p_lds[4][4 * 64];   // P from role A to role B, per pair
   __shared__ __attribute__((aligned(8))) uint8_t flags8[kKvMaxTiles];
   __shared__ uint16_t klist[kKvMaxTiles + kListPad];
@@ -713,7 +756,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       if (nk == 0) continue;
       const int nitems = nk * group;   // (kept tile, query head of the group), head fastest
 
-      // role A's loads of item `item` into buffer item % 3, one at a time
+      // role A's loads of item `item` into buffer item % kBufs, one at a time
       // (load n = 0 .. kLoads of this wave), so that they can go out between
       // the MFMAs of its matrix phase
       struct Plan {
@@ -722,7 +765,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       };
       auto plan = [&](int item) __attribute__((always_inline)) -> Plan {
         Plan pl;
-        const int slot = item % 3;
+        const int slot = item % kBufs;
         const int u = item / group;
         const int h = hk * group + (item - u * group);
         const int j = klist[u] & 0x7fff;
@@ -756,36 +799,38 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       // previous item (B operand of dV) or its bf16 dS (B operand of dK).
       f32x16 sx = {};
       bf16x8 bx0 = {}, bx1 = {};
+      bf16x8 bfr[kPf + 1];   // the leading stream's first fragments, read before its phase opens
 
       // role A on the matrix cores: S(k) when WS, then dV(k - 1) when WV
       auto a_mfma = [&](int k, auto ws, auto wv) __attribute__((always_inline)) {
         constexpr bool kS = decltype(ws)::value, kV = decltype(wv)::value;
         constexpr int kNs = kS ? C::kKSteps : 0;
         constexpr int kN = kNs + (kV ? 2 * C::kDTiles : 0);
-        // rowf points at buffer k % 3 (Q(k)), trf at buffer (k - 1) % 3 (dO(k - 1))
+        // rowf points at buffer k % kBufs (Q(k)), trf at buffer (k - 1) % kBufs (dO(k - 1))
         const __bf16* qt_l = &q_lds[0][0];
         const __bf16* gt_l = &g_lds[0][0];
-        const bool more = k + 1 < nitems;
-        const Plan pl = plan(more ? k + 1 : k);
-        // load n of item k + 1 goes out after MFMA 1 + 3n: the address unit
+        const bool more = k + 2 < nitems;
+        const Plan pl = plan(more ? k + 2 : k);
+        // load n of item k + 2 goes out after MFMA 1 + 3n: the address unit
         // drains while the matrix cores work instead of stalling a vector phase
-        mfma_stream_side<kN, kV ? 2 : 1>(
-            [&](int m) {
-              if (m < kNs) return rowf.get(qt_l, m);
-              const int mm = m - kNs;
-              return trf.get(gt_l, mm / C::kDTiles, mm % C::kDTiles);
-            },
-            [&](int m, const bf16x8& f) {
-              if (m < kNs) {
-                sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, rf[m], m == 0 ? f32x16{} : sx, 0, 0, 0);
-              } else {
-                const int mm = m - kNs, dt = mm % C::kDTiles;
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, mm < C::kDTiles ? bx0 : bx1, acc[dt], 0, 0, 0);
-              }
-            },
-            [&](int m) {
-              if (more && m % 3 == 1 && m / 3 <= kLoads) load_n(pl, m / 3);
-            });
+        auto fetch = [&](int m) {
+          if (m < kNs) return rowf.get(qt_l, m);
+          const int mm = m - kNs;
+          return trf.get(gt_l, mm / C::kDTiles, mm % C::kDTiles);
+        };
+        auto mma = [&](int m, const bf16x8& f) {
+          if (m < kNs) {
+            sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, rf[m], m == 0 ? f32x16{} : sx, 0, 0, 0);
+          } else {
+            const int mm = m - kNs, dt = mm % C::kDTiles;
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, mm < C::kDTiles ? bx0 : bx1, acc[dt], 0, 0, 0);
+          }
+        };
+        auto side = [&](int m) {
+          if (more && m % 3 == 1 && m / 3 <= kLoads) load_n(pl, m / 3);
+        };
+        if constexpr (kS) mfma_stream_side_pre<kN, kV ? 2 : 1>(bfr, fetch, mma, side);
+        else mfma_stream_side<kN, kV ? 2 : 1>(fetch, mma, side);
         // the loads a short stream had no room for
         if (more) {
 #pragma unroll
@@ -800,7 +845,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       // their latencies overlap; the P stores stay spread over the phase, one per group of four,
       // so that they do not arrive at the LDS as one burst beside role B's operand reads.
       auto a_valu = [&](int k) __attribute__((always_inline)) {
-        const int slot = k % 3;
+        const int slot = k % kBufs;
         const int e = __builtin_amdgcn_readfirstlane((int)klist[k / group]);
         float4 l2[4];
   #pragma unroll
@@ -846,28 +891,37 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       auto b_mfma = [&](int k, auto wp, auto wk) __attribute__((always_inline)) {
         constexpr bool kP = decltype(wp)::value, kK = decltype(wk)::value;
         constexpr int kNp = kP ? C::kKSteps : 0;
-        // rowf points at buffer k % 3 (dO(k)), trf at buffer (k - 1) % 3 (Q(k - 1))
+        // rowf points at buffer k % kBufs (dO(k)), trf at buffer (k - 1) % kBufs (Q(k - 1))
         const __bf16* gt_l = &g_lds[0][0];
         const __bf16* qt_l = &q_lds[0][0];
-        mfma_stream<kNp + (kK ? 2 * C::kDTiles : 0), kK ? 2 : 1>(
-            [&](int m) {
-              if (m < kNp) return rowf.get(gt_l, m);
-              const int mm = m - kNp;
-              return trf.get(qt_l, mm / C::kDTiles, mm % C::kDTiles);
-            },
-            [&](int m, const bf16x8& f) {
-              if (m < kNp) {
-                sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, rf[m], m == 0 ? f32x16{} : sx, 0, 0, 0);
-              } else {
-                const int mm = m - kNp, dt = mm % C::kDTiles;
-                acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, mm < C::kDTiles ? bx0 : bx1, acc[dt], 0, 0, 0);
-              }
-            });
+        auto fetch = [&](int m) {
+          if (m < kNp) return rowf.get(gt_l, m);
+          const int mm = m - kNp;
+          return trf.get(qt_l, mm / C::kDTiles, mm % C::kDTiles);
+        };
+        auto mma = [&](int m, const bf16x8& f) {
+          if (m < kNp) {
+            sx = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, rf[m], m == 0 ? f32x16{} : sx, 0, 0, 0);
+          } else {
+            const int mm = m - kNp, dt = mm % C::kDTiles;
+            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f, mm < C::kDTiles ? bx0 : bx1, acc[dt], 0, 0, 0);
+          }
+        };
+        if constexpr (kP) mfma_stream_pre<kNp + (kK ? 2 * C::kDTiles : 0), kK ? 2 : 1>(bfr, fetch, mma);
+        else mfma_stream<kNp + (kK ? 2 * C::kDTiles : 0), kK ? 2 : 1>(fetch, mma);
+      };
+      // the first fragments of the next matrix phase's leading stream, read before the barrier that opens
+      // it: role A's S(k + 1) (Q(k + 1), visible since the barrier that opened phase 2k), role B's
+      // dP(k) (dO(k), visible since the barrier that opened phase 2k - 2); rowf already points at them
+      auto prefetch = [&]() __attribute__((always_inline)) {
+        const __bf16* t = kA ? &q_lds[0][0] : &g_lds[0][0];
+#pragma unroll
+        for (int m = 0; m < kPf; ++m) bfr[m] = rowf.get(t, m);
       };
 
       // role B: dS(k) = P(k) * (dP(k) - Dvec(k))
       auto b_valu = [&](int k) __attribute__((always_inline)) {
-        const int slot = k % 3;
+        const int slot = k % kBufs;
         float ds[16];
   #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -886,27 +940,33 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       // last (k = nitems) have no previous or no current item
       auto phases = [&](int k, auto first, auto last) __attribute__((always_inline)) {
         constexpr bool kFirst = decltype(first)::value, kLast = decltype(last)::value;
-        // advance the fragment offsets one buffer: rowf to k % 3, trf to (k - 1) % 3 (back by two at
-        // the wrap), so that every operand read of the matrix phases is a lane register plus an
-        // immediate offset
+        // advance the fragment offsets one buffer (back by kBufs - 1 at the wrap), so that every
+        // operand read of the matrix phases is a lane register plus an immediate offset: trf to
+        // (k - 1) % kBufs and, in role B, rowf to k % kBufs (role A moved its rowf when it read
+        // ahead in the previous phase pair)
         if (!kFirst) {
-          const int sk = k % 3;
-          rowf.shift(sk == 0 ? -2 * kTileElems : kTileElems);
-          trf.shift(sk == 1 ? -2 * kTileElems : kTileElems);
+          const int sk = k % kBufs;
+          if (!kA) rowf.shift(sk == 0 ? -(kBufs - 1) * kTileElems : kTileElems);
+          trf.shift(sk == 1 ? -(kBufs - 1) * kTileElems : kTileElems);
         }
-        // phase 2k: A on the matrix cores, B on the vector ALU (+ loads of item k + 1)
+        // phase 2k: A on the matrix cores (+ loads of item k + 2), B on the vector ALU
         if (kA) {
           a_mfma(k, std::integral_constant<bool, !kLast>{}, std::integral_constant<bool, !kFirst>{});
         } else {
           if (!kFirst) b_valu(k - 1);
+          if (!kLast) prefetch();
         }
         __builtin_amdgcn_sched_barrier(0);
         bar();
         // phase 2k+1: A on the vector ALU, B on the matrix cores
         if (kA) {
+          if (k + 1 < nitems) {   // the next phase pair opens with S(k + 1): its first reads go out now
+            rowf.shift((k + 1) % kBufs == 0 ? -(kBufs - 1) * kTileElems : kTileElems);
+            prefetch();
+          }
           if (!kLast) a_valu(k);
           __builtin_amdgcn_sched_barrier(0);
-          vm_wait<0>();   // the loads of item k + 1 have landed
+          vm_wait<0>();   // the loads of item k + 2 have landed
         } else {
           b_mfma(k, std::integral_constant<bool, !kLast>{}, std::integral_constant<bool, !kFirst>{});
           __builtin_amdgcn_sched_barrier(0);
@@ -914,18 +974,24 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
         bar();
       };
 
-      // fragment offsets of item 0: rowf at buffer 0, trf at buffer 2 (= (0 - 1) mod 3)
+      // fragment offsets of item 0: rowf at buffer 0, trf at buffer kBufs - 1 (= (0 - 1) mod kBufs)
       rowf.init(ql, hh);
       trf.init(lane);
-      trf.shift(2 * kTileElems);
-      // prologue: item 0 in LDS
+      trf.shift((kBufs - 1) * kTileElems);
+      // prologue: items 0 and 1 in LDS
       if (kA) {
         const Plan p0 = plan(0);
 #pragma unroll
         for (int n = 0; n <= kLoads; ++n) load_n(p0, n);
+        if (nitems > 1) {
+          const Plan p1 = plan(1);
+#pragma unroll
+          for (int n = 0; n <= kLoads; ++n) load_n(p1, n);
+        }
       }
       vm_wait<0>();
       bar();
+      if (kA) prefetch();   // S(0) opens the first phase
       phases(0, std::true_type{}, std::false_type{});
       for (int k = 1; k < nitems; ++k) phases(k, std::false_type{}, std::false_type{});
       phases(nitems, std::false_type{}, std::true_type{});
