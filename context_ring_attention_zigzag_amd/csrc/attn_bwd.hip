@@ -758,19 +758,23 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
 
       // role A's loads of item `item` into buffer item % kBufs, one at a time
       // (load n = 0 .. kLoads of this wave), so that they can go out between
-      // the MFMAs of its matrix phase
+      // the MFMAs of its matrix phase. They are issued whether or not the item
+      // exists, so that the matrix phase is one branch-free block
       struct Plan {
         i32x4 rs, rx;
         uint32_t dst, dx;
       };
-      auto plan = [&](int item) __attribute__((always_inline)) -> Plan {
+      // valid false: there is no such item; the descriptors are empty (the loads write zeros into its
+      // buffer, which nothing reads), and the addresses come from item 0's list entry
+      auto plan = [&](int item, bool valid) __attribute__((always_inline)) -> Plan {
         Plan pl;
         const int slot = item % kBufs;
-        const int u = item / group;
-        const int h = hk * group + (item - u * group);
+        const int ia = valid ? item : 0;
+        const int u = ia / group;
+        const int h = hk * group + (ia - u * group);
         const int j = klist[u] & 0x7fff;
         const int q0 = (seg0 + j) * kT;
-        const uint32_t rows = (uint32_t)min(kT, a.Lq - q0);
+        const uint32_t rows = valid ? (uint32_t)min(kT, a.Lq - q0) : 0u;
         const __bf16* base = load_q
             ? static_cast<const __bf16*>(a.q) + b * a.q_sb + h * a.q_sh + (int64_t)q0 * a.q_sl
             : static_cast<const __bf16*>(a.dout) + b * a.do_sb + h * a.do_sh + (int64_t)q0 * a.do_sl;
@@ -809,8 +813,7 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
         // rowf points at buffer k % kBufs (Q(k)), trf at buffer (k - 1) % kBufs (dO(k - 1))
         const __bf16* qt_l = &q_lds[0][0];
         const __bf16* gt_l = &g_lds[0][0];
-        const bool more = k + 2 < nitems;
-        const Plan pl = plan(more ? k + 2 : k);
+        const Plan pl = plan(k + 2, k + 2 < nitems);
         // load n of item k + 2 goes out after MFMA 1 + 3n: the address unit
         // drains while the matrix cores work instead of stalling a vector phase
         auto fetch = [&](int m) {
@@ -827,16 +830,14 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
           }
         };
         auto side = [&](int m) {
-          if (more && m % 3 == 1 && m / 3 <= kLoads) load_n(pl, m / 3);
+          if (m % 3 == 1 && m / 3 <= kLoads) load_n(pl, m / 3);
         };
         if constexpr (kS) mfma_stream_side_pre<kN, kV ? 2 : 1>(bfr, fetch, mma, side);
         else mfma_stream_side<kN, kV ? 2 : 1>(fetch, mma, side);
         // the loads a short stream had no room for
-        if (more) {
 #pragma unroll
-          for (int n = 0; n <= kLoads; ++n)
-            if (3 * n + 1 >= kN) load_n(pl, n);
-        }
+        for (int n = 0; n <= kLoads; ++n)
+          if (3 * n + 1 >= kN) load_n(pl, n);
       };
 
       // role A: P(k) = 2^(S(k) c - lse2(k)), masked; to LDS for role B, bf16 kept for dV(k).
@@ -980,13 +981,12 @@ __global__ void __launch_bounds__(kKvThreads, 1) bwd_dkv_kernel(BwdArgs a) {
       trf.shift((kBufs - 1) * kTileElems);
       // prologue: items 0 and 1 in LDS
       if (kA) {
-        const Plan p0 = plan(0);
+        const Plan p0 = plan(0, true);
+        const Plan p1 = plan(1, nitems > 1);
 #pragma unroll
-        for (int n = 0; n <= kLoads; ++n) load_n(p0, n);
-        if (nitems > 1) {
-          const Plan p1 = plan(1);
-#pragma unroll
-          for (int n = 0; n <= kLoads; ++n) load_n(p1, n);
+        for (int n = 0; n <= kLoads; ++n) {
+          load_n(p0, n);
+          load_n(p1, n);
         }
       }
       vm_wait<0>();
