@@ -19,7 +19,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import re
 import sys
@@ -37,7 +36,7 @@ KERNEL_SRCS = [os.path.join(ROOT, "context_ring_attention_zigzag_amd", "csrc", f
 KERNEL_NAME = "attn_bf16_kernel"
 
 
-def allowed_pairs(w, s_pad: int, lq: int, q_pos, k_pos_all) -> int:
+def allowed_pairs(w, q_pos, k_pos_all) -> int:
     """Allowed (query, key) pairs of one (b, h), counted from the position arrays."""
     import numpy as np
     q = q_pos[q_pos >= 0]
@@ -169,7 +168,7 @@ def measure_state_kernels(cpr, torch, B: int, H: int, Lq: int, D: int, out_dtype
     return res
 
 
-def layout_balance(args, cpr, di, torch, np, w, gen_slice, lay_codes):
+def layout_balance(args, cpr, di, torch, w, gen_slice, lay_codes):
     """Per-rank time of the fused ring pass for each layout at one causal workload shape.
 
     The causal split is what the layouts are about: a contiguous split leaves
@@ -191,7 +190,7 @@ def layout_balance(args, cpr, di, torch, np, w, gen_slice, lay_codes):
             ri = di.prepare_rank(nat["q"], nat["k"], nat["v"], w.S, w.cp, lay, rank, tok, pos)
             o = torch.empty_like(ri.q_local)
             lse = torch.empty(ri.q_local.shape[:3], dtype=torch.float32, device="cuda")
-            pairs = allowed_pairs(w, ri.s_pad, ri.lq, ri.q_pos.cpu().numpy(), ri.ring_pos.cpu().numpy())
+            pairs = allowed_pairs(w, ri.q_pos.cpu().numpy(), ri.ring_pos.cpu().numpy())
 
             def run():
                 cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, True, 0.0,
@@ -219,7 +218,7 @@ def layout_balance(args, cpr, di, torch, np, w, gen_slice, lay_codes):
                       "data": "synthetic: seeded N(0,1) draws per (tensor, b, h) slice"}), flush=True)
 
 
-def bench_backward(args, cpr, di, torch, np, w, gen_slice, lay_codes):
+def bench_backward(args, cpr, di, torch, w, gen_slice, lay_codes):
     """Time one rank's backward ring pass: preprocessing, dQ over every block, the rank's share of every
     block's dK and dV. Inputs: the same seeded Q, K, V as the forward measurement plus a seeded dO; O and
     LSE from the library's own forward pass (timing only, nothing is checked here)."""
@@ -242,7 +241,7 @@ def bench_backward(args, cpr, di, torch, np, w, gen_slice, lay_codes):
     split = ws_bytes > cpr.cp_ring_attn_bwd_workspace_size(w.B, w.H, ri.lq)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
-    pairs = allowed_pairs(w, ri.s_pad, ri.lq, ri.q_pos.cpu().numpy(), ri.ring_pos.cpu().numpy())
+    pairs = allowed_pairs(w, ri.q_pos.cpu().numpy(), ri.ring_pos.cpu().numpy())
     # FlashAttention convention: the backward is 2.5 forward passes (S recomputed, dP, dV, dQ, dK)
     flop = 10.0 * w.B * w.H * w.D * pairs
     stream = torch.cuda.current_stream()
@@ -330,12 +329,12 @@ def main():
 
     LAY_CODES = {"zigzag": cpr.ZIGZAG, "contiguous": cpr.CONTIGUOUS, "striped": cpr.STRIPED}
     if args.layout_balance:
-        layout_balance(args, cpr, di, torch, np, WORKLOADS["seq32k_cp4"], gen_slice, LAY_CODES)
+        layout_balance(args, cpr, di, torch, WORKLOADS["seq32k_cp4"], gen_slice, LAY_CODES)
         return
 
     w = WORKLOADS[args.workload]
     if args.which == "backward":
-        bench_backward(args, cpr, di, torch, np, w, gen_slice, LAY_CODES)
+        bench_backward(args, cpr, di, torch, w, gen_slice, LAY_CODES)
         return
     rank = w.ranks[0] if args.rank is None else args.rank
     lay = LAY_CODES[w.layout]
@@ -358,7 +357,7 @@ def main():
     t_prep = time.perf_counter() - t_prep
 
     pos_h = ri.ring_pos.cpu().numpy()
-    pairs = allowed_pairs(w, ri.s_pad, ri.lq, ri.q_pos.cpu().numpy(), pos_h)
+    pairs = allowed_pairs(w, ri.q_pos.cpu().numpy(), pos_h)
     flop = 4.0 * w.B * w.H * w.D * pairs
 
     stream = torch.cuda.current_stream()

@@ -108,12 +108,12 @@ def sample_rows(n_local: int, chunk: int, count: int, seed: int) -> np.ndarray:
     return np.array(sorted(picks), dtype=np.int64)
 
 
-def packed_windows(doc_lens, causal: bool):
+def packed_windows(doc_lens):
     """Key-position windows of a packed sequence, in natural token order.
 
     Documents of the given lengths are packed back to back; token t of the
-    document [a, a + n) may attend keys at positions [a, a + n - 1] (the causal
-    bound, when asked for, is applied by the attention itself). Returns int32
+    document [a, a + n) may attend keys at positions [a, a + n - 1]; a causal
+    bound, when wanted, is applied by the attention itself. Returns int32
     (lo, hi) arrays of sum(doc_lens) entries. Input metadata only: both the
     HIP path and the oracle consume it.
     """

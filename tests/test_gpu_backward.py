@@ -77,7 +77,7 @@ class Case:
         self.lq = self.s_pad // cp
         self.lo_nat = self.hi_nat = None
         if docs is not None:
-            self.lo_nat, self.hi_nat = packed_windows(docs, causal)
+            self.lo_nat, self.hi_nat = packed_windows(docs)
         if windows is not None:
             self.lo_nat, self.hi_nat = (np.asarray(x, dtype=np.int64) for x in windows)
 

@@ -239,7 +239,7 @@ def test_packed_documents(case):
     assert sum(docs) == S
     w = small_workload("docs", dtype, 1, 2, D, S, cp, layout, causal, seed=zlib.crc32(repr(case).encode()) % 1000)
     dev, host = natural_inputs(w)
-    lo, hi = packed_windows(docs, causal)
+    lo, hi = packed_windows(docs)
     for r in range(cp):
         ro, rl = oracle.rank_reference(host["q"], host["k"], host["v"], S, cp, ORACLE_LAYS[layout], r, causal,
                                        kw_lo_nat=lo, kw_hi_nat=hi)
@@ -259,7 +259,7 @@ def test_mid_size_grouped_heads_documents_padded(layout):
     dev, host = natural_inputs(w)
     k_nat, v_nat = dev["k"][:, :H_kv].contiguous(), dev["v"][:, :H_kv].contiguous()
     hk, hv = host["k"][:, :H_kv], host["v"][:, :H_kv]
-    lo, hi = packed_windows(docs, True)
+    lo, hi = packed_windows(docs)
     for r in (0, 3):
         ro, rl = oracle.rank_reference(host["q"], hk, hv, w.S, w.cp, ORACLE_LAYS[layout], r, True,
                                        kw_lo_nat=lo, kw_hi_nat=hi)
@@ -501,7 +501,7 @@ def test_seq32k_grouped_heads_packed_documents_sampled():
     w = small_workload("gqa_docs_32k", "bf16", 1, H, 128, 32768, 4, "zigzag", True, seed=31, ranks=(3,))
     docs = (5000, 12000, 768, 9000, 6000)
     assert sum(docs) == w.S
-    lo, hi = packed_windows(docs, True)
+    lo, hi = packed_windows(docs)
     lq = w.S // w.cp
     rows = sample_rows(lq, lq // 2, 64, seed=w.seed)
     q_nat = torch.empty((1, H, w.S, w.D), dtype=torch.bfloat16, device="cuda")

@@ -403,7 +403,7 @@ def test_packed_documents_equal_separate_attention(causal):
     docs = [5, 9, 1, 16, 3]
     s, d = sum(docs), 4
     q, k, v = rnd((1, 2, s, d), 80), rnd((1, 2, s, d), 81), rnd((1, 2, s, d), 82)
-    lo, hi = packed_windows(docs, causal)
+    lo, hi = packed_windows(docs)
     pos = np.arange(s)
     o, lse = oracle.full_attention(q, k, v, pos, pos, causal, kw_lo=lo, kw_hi=hi)
     a = 0
@@ -436,7 +436,7 @@ def test_ring_emulation_with_gqa_and_documents(layout):
     s = sum(docs)
     lay = LAYOUTS[layout]
     q, k, v = rnd((1, h, s, d), 93), rnd((1, h_kv, s, d), 94), rnd((1, h_kv, s, d), 95)
-    lo_nat, hi_nat = packed_windows(docs, True)
+    lo_nat, hi_nat = packed_windows(docs)
     tok, pos = oracle.layout(s, cp, lay)
     s_pad, lr = len(tok), len(tok) // cp
     real = tok < s
@@ -576,7 +576,7 @@ def test_backward_vs_torch_autograd(causal, h_kv):
 def test_backward_with_windows_vs_torch_autograd():
     docs, h, d = [5, 11, 2, 9], 2, 6
     s = sum(docs)
-    lo, hi = packed_windows(docs, True)
+    lo, hi = packed_windows(docs)
     hi = np.minimum(hi, np.arange(s))
     lo = np.maximum(lo, np.arange(s) - 4)             # plus a sliding window of 5 keys
     q, k, v, do = (rnd((1, h, s, d), 104 + i) for i in range(4))
@@ -692,7 +692,7 @@ def test_ring_backward_with_gqa_and_documents(layout):
     s = sum(docs)
     q, do = rnd((1, h, s, d), 130), rnd((1, h, s, d), 131)
     k, v = rnd((1, h_kv, s, d), 132), rnd((1, h_kv, s, d), 133)
-    lo, hi = packed_windows(docs, True)
+    lo, hi = packed_windows(docs)
     dq, dk, dv, _ = ring_backward_all_ranks(q, k, v, do, s, cp, LAYOUTS[layout], True, lo, hi)
     nat = np.arange(s)
     want = oracle.attention_backward(q, k, v, do, nat, nat, True, kw_lo=lo, kw_hi=hi)
