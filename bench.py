@@ -284,12 +284,15 @@ def bench_backward(args, cpr, di, torch, w, gen_slice, lay_codes):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="longdoc_noncausal")
-    ap.add_argument("--rank", type=int, default=None)
-    ap.add_argument("--stepwise", action="store_true", help="time the init/step/finalize path instead of the fused one")
+    ap.add_argument("--gpus", type=int, default=1, help="GPUs of the run; only 1 is supported")
+    ap.add_argument("--steps", type=int, default=20, help="timed passes")
+    ap.add_argument("--warmup", type=int, default=3, help="untimed passes before them")
+    ap.add_argument("--workload", default="longdoc_noncausal",
+                    help="longdoc_noncausal (default), seq32k_cp4, million_cp8, example_4k, ...")
+    ap.add_argument("--rank", type=int, default=None, help="the rank to emulate (default: the workload's)")
+    ap.add_argument("--stepwise", action="store_true",
+                    help="time the stepwise run (one step launch per ring block, the first from the empty state, "
+                         "the last writing the output) instead of the fused one")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--layout-balance", action="store_true",
                     help="time every rank of the 32k-token causal sequence under the contiguous, zigzag and striped "
