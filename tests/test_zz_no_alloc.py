@@ -90,6 +90,44 @@ def test_noalloc_large_grid_runs_unsplit():
     assert not split_engaged(w.B, w.H, ri.lq, w.D)
 
 
+def test_noalloc_grouped_heads_and_key_windows():
+    """Grouped-query heads (4 query heads on 2 K/V heads) and sliding key windows with some empty ones, on a grid
+    small enough to split: the extension argument reaches the split kernels through the scratch path too."""
+    w = small_workload("noalloc_gqa_win", "bf16", 1, 4, 128, 2048, 2, "zigzag", True, seed=504)
+    host = {t: gen_tensor(w, t) for t in "qkv"}
+    host["k"], host["v"] = host["k"][:, :2].copy(), host["v"][:, :2].copy()
+    dev = {t: torch.from_numpy(host[t]).to(torch.bfloat16).cuda() for t in "qkv"}
+    t = np.arange(w.S)
+    lo_nat = np.maximum(t - 300, 0).astype(np.int32)
+    hi_nat = np.where(t % 9 == 4, lo_nat - 1, t).astype(np.int32)
+    for rank in range(w.cp):
+        ri = di.prepare_rank(dev["q"], dev["k"], dev["v"], w.S, w.cp, cpr.ZIGZAG, rank)
+        assert split_engaged(w.B, w.H, ri.lq, w.D)
+        tok = ri.token_idx[rank * ri.lq:(rank + 1) * ri.lq].long()
+        real = tok < w.S
+        kw = [torch.where(real, torch.from_numpy(nat).cuda()[tok.clamp(max=w.S - 1)], 0).to(torch.int32).contiguous()
+              for nat in (lo_nat, hi_nat)]
+        ws = torch.empty(cpr.cp_ring_attn_workspace_size(w.B, w.H, ri.lq, w.D), dtype=torch.uint8, device="cuda")
+        o_ws, lse_ws = torch.empty_like(ri.q_local), torch.empty(ri.q_local.shape[:3], device="cuda")
+        cpr.cp_ring_attn_run(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, True, 0.0, o_ws,
+                             lse_ws, ws, kw_lo=kw[0], kw_hi=kw[1])
+        o_na = torch.full_like(ri.q_local, float("nan"))
+        lse_na = torch.full(ri.q_local.shape[:3], float("nan"), device="cuda")
+        cpr.cp_ring_attn_run_noalloc(ri.q_local, ri.q_pos, ri.k_ring, ri.v_ring, ri.ring_pos, w.cp, rank, True, 0.0,
+                                     o_na, lse_na, kw_lo=kw[0], kw_hi=kw[1])
+        torch.cuda.synchronize()
+        a, b = o_ws.float().cpu().numpy(), o_na.float().cpu().numpy()
+        la, lb = lse_ws.cpu().numpy(), lse_na.cpu().numpy()
+        note(f"{w.name} rank {rank}: bit-identical O {np.array_equal(a, b)}, LSE {np.array_equal(la, lb)}")
+        assert np.array_equal(a, b) and np.array_equal(la, lb)
+        ro, rl = oracle.rank_reference(*(host[x].astype(np.float64) for x in "qkv"), w.S, w.cp, oracle.ZIGZAG, rank,
+                                       True, kw_lo_nat=lo_nat, kw_hi_nat=hi_nat)
+        assert np.isneginf(rl).any() and np.array_equal(np.isneginf(rl), np.isneginf(lb))
+        fin = np.isfinite(rl)
+        assert float(np.abs(b - ro).max()) <= TOL_O
+        assert float(np.abs(lb[fin] - rl[fin]).max()) <= TOL_L
+
+
 def test_noalloc_rejects_bad_arguments():
     q = torch.zeros(1, 2, 64, 128, dtype=torch.bfloat16, device="cuda")
     pos = torch.zeros(64, dtype=torch.int32, device="cuda")
