@@ -167,6 +167,14 @@ def test_bwd_gqa(dtype, h, h_kv, d):
     run_case(c, (0, 1), f"{dtype}_gqa_{h}_{h_kv}")
 
 
+@pytest.mark.parametrize("layout,causal,h,h_kv,S,cp", [("striped", True, 4, 2, 384, 3), ("contiguous", False, 2, 2, 301, 2)])
+def test_bwd_f32_head_dim_128(layout, causal, h, h_kv, S, cp):
+    """The float32 backward kernels at D = 128 (the other float32 cases run at D = 64): grouped heads under the
+    striped causal layout, and a non-causal contiguous case with a padded tail."""
+    c = Case("f32", 1, h, h_kv, 128, S, cp, layout, causal, seed=330 + S)
+    run_case(c, range(cp), f"f32_d128_{layout}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_bwd_packed_documents(dtype):
     """Per-query document windows (packed sequences) with grouped-query heads and striped layout."""

@@ -207,6 +207,7 @@ GQA = [
     ("bf16", 64, 513, 2, "contiguous", False, 4, 1),
     ("f32", 64, 201, 3, "striped", True, 6, 3),
     ("bf16", 128, 700, 3, "striped", True, 4, 2),
+    ("f32", 128, 300, 2, "zigzag", True, 4, 2),
 ]
 
 
